@@ -1,0 +1,19 @@
+"""CPU oracle for the FP8 W8A8 scaled GEMM, its quantizers and the FP8 KV cache.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow reference that the
+HIP path is checked against.  It shares no code with the HIP library and does
+not import it.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import, call, link or run anything here; the
+product path never does, and must fail loudly rather than fall back to it.
+
+Modules:
+  fp8    -- E4M3 / E5M2 formats, saturating round-to-nearest-even encoder,
+            bf16 rounding
+  w8a8   -- per-token, per-tensor and per-channel quantizers; exact GEMM
+            accumulator and scaled bf16 output
+  kv     -- KV-cache calibrate / quantize / dequantize / append
+  native -- the same encoder in plain C (oracle/c/fp8_oracle.c) for sweeps
+            over every float32 bit pattern; loaded from its built library
+"""
+
+from . import fp8, kv, w8a8  # noqa: F401
