@@ -1,0 +1,204 @@
+/*
+ * fp8sg — FP8 W8A8 scaled GEMM, FP8 quantizers and FP8 KV-cache passes for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Every pointer argument is a DEVICE pointer (memory on the current HIP
+ *   device), except where stated.  The caller allocates and frees every buffer;
+ *   the library allocates no memory and keeps no per-call state.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *   work is enqueued asynchronously on it; results are visible after the caller
+ *   synchronises the stream.  Scales live in device memory, so calls do not
+ *   synchronise with the host.
+ * - Tensors are dense and row-major (last extent contiguous).  Data pointers
+ *   must be 16-byte aligned; scale pointers 4-byte aligned.
+ * - FP8 data travels as raw bytes (uint8): E4M3 is the OCP "fn" variant
+ *   (bias 7, max 448, no infinities, S.1111.111 = NaN); E5M2 has bias 15,
+ *   max 57344, infinities and NaNs.
+ * - Quantization follows one rule everywhere: the stored scale s is the
+ *   dequantization factor (value ~ s * code); a value x is encoded as
+ *   FMT(RN32(x / s)), the IEEE-754 binary32 quotient rounded to the nearest FP8
+ *   value, ties to even, saturating at +-max (also for +-inf); the sign of zero
+ *   is kept; NaN gives a NaN code.  A dynamic scale is s = RN32(amax / max),
+ *   or 1.0 when that is 0.  Quantized codes and scales are bit-exact with this
+ *   rule.  (FP8 Inference Explained, in depth -- "The numbers in one byte",
+ *   "Scales and their granularity"; Quantization: FP8 inference and KV-cache
+ *   quantization -- "Dynamic scales or static scales".)
+ * - Errors: arguments are checked synchronously, before any HIP call, and a
+ *   non-OK status is returned with nothing enqueued.  No C++ exception crosses
+ *   the ABI.  Work of size 0 (M == 0, numel == 0, ...) returns FP8SG_OK without
+ *   launching.  Faults inside a kernel surface at the caller's stream
+ *   synchronisation.
+ * - Inputs containing NaN or infinity are out of contract for the dynamic
+ *   (amax-based) paths, whose scale would itself be non-finite.
+ */
+#ifndef FP8SG_H
+#define FP8SG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8sg_status {
+    FP8SG_OK = 0,
+    FP8SG_E_NULL = 1,       /* a required pointer is NULL                              */
+    FP8SG_E_SHAPE = 2,      /* a size is negative, too large, or breaks a multiple-of rule */
+    FP8SG_E_ALIGN = 3,      /* a pointer is not aligned as required                    */
+    FP8SG_E_DTYPE = 4,      /* unsupported dtype / format / mode value                 */
+    FP8SG_E_DEVICE = 5,     /* no HIP device, or the current device is not gfx950      */
+    FP8SG_E_LAUNCH = 6,     /* a kernel launch failed (hipGetLastError)                */
+    FP8SG_E_WORKSPACE = 7   /* workspace missing or smaller than the size query says   */
+} fp8sg_status;
+
+typedef enum fp8sg_dtype {
+    FP8SG_F32 = 0,
+    FP8SG_BF16 = 1,
+    FP8SG_E4M3 = 2,
+    FP8SG_E5M2 = 3
+} fp8sg_dtype;
+
+/* How the activation scale of fp8_scaled_gemm is organised. */
+typedef enum fp8sg_scale_mode {
+    FP8SG_SCALE_PER_TOKEN = 0,   /* one fp32 scale per row of A ([M])   */
+    FP8SG_SCALE_PER_TENSOR = 1   /* one fp32 scale for all of A ([1])   */
+} fp8sg_scale_mode;
+
+/* How fp8_scaled_gemm accumulates the FP8 x FP8 products. */
+typedef enum fp8sg_accum {
+    /* Products formed exactly and summed in fp32 (the FP8 codes are widened
+     * exactly to bf16 and multiplied on the bf16 matrix cores).  The
+     * accumulator meets |acc - exact| <= 1e-5 * sum_k |a_k w_k|. */
+    FP8SG_ACCUM_EXACT = 0,
+    /* Native FP8 matrix cores.  On gfx950 each instruction sums its products in
+     * groups of 8 consecutive k, aligning them to the group's largest product
+     * and truncating below 2^(e_max - 13); group sums are then added in fp32.
+     * Twice the peak rate of FP8SG_ACCUM_EXACT, with that error. */
+    FP8SG_ACCUM_MFMA_FP8 = 1
+} fp8sg_accum;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp8sg_status_string(int status);
+
+/* Library ABI version (incremented on any signature change). */
+int fp8sg_version(void);
+
+/*
+ * Dynamic per-token activation quantization (one scale per row).
+ * FP8 Inference Explained, in depth -- "Inside a quantized linear layer": a
+ * small kernel finds each token's amax, divides and casts to E4M3; "Dynamic
+ * scales or static scales" on the KV-cache page: each token's maximum lands on
+ * 448.
+ *   x       [M, K] input, x_dtype FP8SG_BF16 or FP8SG_F32
+ *   q       [M, K] E4M3 codes (output)
+ *   scales  [M] fp32, s_i = RN32(max_k |x_ik| / 448) or 1.0 (output)
+ *   K % 16 == 0; M, K >= 0.
+ */
+fp8sg_status fp8_quant_per_token(const void* x, int x_dtype, int64_t M, int64_t K,
+                                 uint8_t* q, float* scales, void* stream);
+
+/*
+ * Static per-tensor quantization with a given scale; values beyond max * s
+ * saturate ("Dynamic scales or static scales": 180 / s = 672 clamps to 448).
+ *   x      [numel] input, FP8SG_BF16 or FP8SG_F32
+ *   scale  [1] fp32 (device), positive and finite
+ *   fmt    FP8SG_E4M3 or FP8SG_E5M2
+ *   q      [numel] codes (output)
+ */
+fp8sg_status fp8_quant_per_tensor_static(const void* x, int x_dtype, int64_t numel, const float* scale,
+                                         int fmt, uint8_t* q, void* stream);
+
+/*
+ * Offline per-output-channel weight quantization: the dynamic row rule applied
+ * to the rows of W (FP8 Inference Explained, in depth -- "Inside a quantized
+ * linear layer": weights stored as E4M3 with one FP32 scale per output channel).
+ *   w         [N, K] FP8SG_F32 or FP8SG_BF16
+ *   wq        [N, K] E4M3 codes (output)
+ *   w_scales  [N] fp32 (output)
+ *   K % 16 == 0.
+ */
+fp8sg_status fp8_quant_weight_per_channel(const void* w, int w_dtype, int64_t N, int64_t K,
+                                          uint8_t* wq, float* w_scales, void* stream);
+
+/*
+ * Bytes of device workspace fp8_scaled_gemm needs for these arguments (0 when
+ * the activation arrives already quantized).  Host-only; no HIP call.
+ */
+size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, int64_t N, int64_t K);
+
+/*
+ * Scaled GEMM  Y = diag(s_a) (A_q W_q^T) diag(s_w), written as bf16 (or fp32).
+ * Both scales are constant along k and leave the sum (FP8 Inference Explained,
+ * in depth -- "Inside a quantized linear layer"); FP8 x FP8 products accumulate
+ * in fp32 (FP8 Quantization notebook -- "How FP8 Matmul Works at the Hardware
+ * Level").
+ *   a             [M, K]: a_dtype FP8SG_E4M3 = codes already quantized;
+ *                 FP8SG_BF16 / FP8SG_F32 = high-precision activations that this
+ *                 call quantizes first (per token, or per tensor with the given
+ *                 scale), writing the codes into the workspace.
+ *   a_scales      per-token: [M] fp32; an input when a is E4M3, an output (the
+ *                 computed dynamic scales) when a is BF16/F32 (may then be NULL).
+ *                 per-tensor: [1] fp32 input in every case.
+ *   a_scale_mode  FP8SG_SCALE_PER_TOKEN or FP8SG_SCALE_PER_TENSOR
+ *   wq            [N, K] E4M3 weight codes, K contiguous (W_q is "B" column-major)
+ *   w_scales      [N] fp32 per-output-channel scales
+ *   y             [M, N] output, y_dtype FP8SG_BF16 (round to nearest even) or
+ *                 FP8SG_F32 (the same epilogue without the bf16 rounding; with
+ *                 unit scales this is the raw accumulator)
+ *   accum         FP8SG_ACCUM_EXACT or FP8SG_ACCUM_MFMA_FP8
+ *   workspace     device buffer of at least fp8_scaled_gemm_workspace_size(...)
+ *                 bytes, 256-byte aligned (may be NULL when that size is 0)
+ *   K % 128 == 0; M, N >= 0 arbitrary.
+ */
+fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode,
+                             const uint8_t* wq, const float* w_scales, void* y, int y_dtype,
+                             int64_t M, int64_t N, int64_t K, int accum,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * KV-cache calibration: one scale per kv head, s_h = RN32(amax_h / max) over
+ * all (b, s, d) of head h, or 1.0 when that is 0 (per-head KV scales require
+ * calibration -- Quantization: FP8 inference and KV-cache quantization,
+ * "Turning it on in an engine").
+ *   kv           [B, S, H, D] bf16 (uint16 bit patterns)
+ *   fmt          FP8SG_E4M3 (max 448) or FP8SG_E5M2 (max 57344)
+ *   head_scales  [H] fp32 (output; also used as scratch during the call)
+ *   D % 16 == 0.
+ */
+fp8sg_status fp8_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,
+                              float* head_scales, void* stream);
+
+/*
+ * KV-cache quantization with per-head scales (FP8 Inference Explained, in
+ * depth -- "FP8 KV cache": stored FP8 halves the cache).
+ *   kv [B, S, H, D] bf16 -> out [B, S, H, D] codes; code = FMT(RN32(x / s_h)).
+ *   D % 16 == 0.
+ */
+fp8sg_status fp8_kv_quant(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D,
+                          const float* head_scales, int fmt, uint8_t* out, void* stream);
+
+/*
+ * KV-cache dequantization: out = bf16(RN32(dec(code) * s_h)) (round to nearest
+ * even).  kvq [B, S, H, D] codes -> out [B, S, H, D] bf16.  D % 16 == 0.
+ */
+fp8sg_status fp8_kv_dequant(const uint8_t* kvq, int64_t B, int64_t S, int64_t H, int64_t D,
+                            const float* head_scales, int fmt, uint16_t* out, void* stream);
+
+/*
+ * Append one token per sequence: kv_new [B, H, D] bf16 is quantized with the
+ * existing per-head scales (saturating) and written to cache[b, pos[b], :, :]
+ * of cache [B, S_cap, H, D]; nothing else is written.  pos [B] int32 (device);
+ * a sequence whose pos[b] lies outside [0, S_cap) is skipped.  D % 16 == 0.
+ */
+fp8sg_status fp8_kv_append(const uint16_t* kv_new, const int32_t* pos, int64_t B, int64_t S_cap,
+                           int64_t H, int64_t D, const float* head_scales, int fmt,
+                           uint8_t* cache, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8SG_H */

@@ -1,0 +1,233 @@
+// C-ABI entry points of libfp8sg: argument validation (always before any HIP
+// call), device check, workspace layout and dispatch to the kernel launchers.
+// The declarations, with the meaning, layout and ownership of every argument,
+// are in include/fp8sg.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/fp8sg.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// 0 = unknown, 1 = gfx950, 2 = not usable.  One slot per device ordinal.
+std::atomic<int> g_dev_state[64];
+
+fp8sg_status device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return FP8SG_E_DEVICE;
+    }
+    if (dev >= 64) return FP8SG_E_DEVICE;
+    int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return FP8SG_E_DEVICE;
+        }
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? FP8SG_OK : FP8SG_E_DEVICE;
+}
+
+fp8sg_status launched(hipError_t e) { return e == hipSuccess ? FP8SG_OK : FP8SG_E_LAUNCH; }
+
+bool is_hp(int dt) { return dt == FP8SG_F32 || dt == FP8SG_BF16; }
+bool is_fp8(int dt) { return dt == FP8SG_E4M3 || dt == FP8SG_E5M2; }
+
+// Row-wise dynamic quantization shared by the per-token and per-channel calls.
+fp8sg_status row_quant(const void* x, int dt, int64_t R, int64_t K, uint8_t* q, float* scales, void* stream) {
+    if (!is_hp(dt)) return FP8SG_E_DTYPE;
+    if (R < 0 || K < 0 || R >= kMaxDim || K >= kMaxDim || (K % 16) != 0) return FP8SG_E_SHAPE;
+    if (R == 0) return FP8SG_OK;
+    if (!scales || (K > 0 && (!x || !q))) return FP8SG_E_NULL;
+    if ((x && !aligned(x, 16)) || (q && !aligned(q, 16)) || !aligned(scales, 4)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    // K == 0 still writes the scales: the maximum of an empty row is 0, so s = 1.0
+    return launched(fp8sg::launch_row_quant(x, dt == FP8SG_BF16, R, K, q, scales, (hipStream_t)stream));
+}
+
+// Common checks for the [B, S, H, D] KV calls.
+fp8sg_status kv_shape(int64_t B, int64_t S, int64_t H, int64_t D, int fmt, int64_t* numel) {
+    if (!is_fp8(fmt)) return FP8SG_E_DTYPE;
+    if (B < 0 || S < 0 || H < 0 || D < 0) return FP8SG_E_SHAPE;
+    if (B >= kMaxDim || S >= kMaxDim || H >= kMaxDim || D >= kMaxDim) return FP8SG_E_SHAPE;
+    if (D % 16 != 0) return FP8SG_E_SHAPE;
+    if (H > 4096) return FP8SG_E_SHAPE;
+    __int128 n = (__int128)B * S * H * D;
+    if (n >= ((__int128)1 << 62)) return FP8SG_E_SHAPE;
+    *numel = (int64_t)n;
+    return FP8SG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8sg_status_string(int status) {
+    switch (status) {
+        case FP8SG_OK: return "ok";
+        case FP8SG_E_NULL: return "required pointer is NULL";
+        case FP8SG_E_SHAPE: return "invalid shape";
+        case FP8SG_E_ALIGN: return "misaligned pointer";
+        case FP8SG_E_DTYPE: return "unsupported dtype, format or mode";
+        case FP8SG_E_DEVICE: return "no gfx950 HIP device";
+        case FP8SG_E_LAUNCH: return "kernel launch failed";
+        case FP8SG_E_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int fp8sg_version(void) { return kAbiVersion; }
+
+fp8sg_status fp8_quant_per_token(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* q, float* scales,
+                                 void* stream) {
+    return row_quant(x, x_dtype, M, K, q, scales, stream);
+}
+
+fp8sg_status fp8_quant_weight_per_channel(const void* w, int w_dtype, int64_t N, int64_t K, uint8_t* wq,
+                                          float* w_scales, void* stream) {
+    return row_quant(w, w_dtype, N, K, wq, w_scales, stream);
+}
+
+fp8sg_status fp8_quant_per_tensor_static(const void* x, int x_dtype, int64_t numel, const float* scale, int fmt,
+                                         uint8_t* q, void* stream) {
+    if (!is_hp(x_dtype) || !is_fp8(fmt)) return FP8SG_E_DTYPE;
+    if (numel < 0 || numel >= ((int64_t)1 << 62)) return FP8SG_E_SHAPE;
+    if (numel == 0) return FP8SG_OK;
+    if (!x || !scale || !q) return FP8SG_E_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    return launched(fp8sg::launch_grouped_quant(x, x_dtype == FP8SG_BF16, numel, scale, 1, 1,
+                                                fmt == FP8SG_E4M3 ? 0 : 1, q, (hipStream_t)stream));
+}
+
+size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, int64_t N, int64_t K) {
+    (void)N;
+    if (!is_hp(a_dtype) || M <= 0 || K < 0) return 0;
+    size_t bytes = align256((size_t)M * (size_t)K);
+    if (a_scale_mode == FP8SG_SCALE_PER_TOKEN) bytes += align256((size_t)M * 4);
+    return bytes;
+}
+
+fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
+                             const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K, int accum,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!(a_dtype == FP8SG_E4M3 || is_hp(a_dtype))) return FP8SG_E_DTYPE;
+    if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
+    if (!(a_scale_mode == FP8SG_SCALE_PER_TOKEN || a_scale_mode == FP8SG_SCALE_PER_TENSOR)) return FP8SG_E_DTYPE;
+    if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (K % 128 != 0) return FP8SG_E_SHAPE;
+    if (M == 0 || N == 0) return FP8SG_OK;
+    if (!y || !w_scales) return FP8SG_E_NULL;
+    if (K > 0 && (!a || !wq)) return FP8SG_E_NULL;
+    const bool per_token = a_scale_mode == FP8SG_SCALE_PER_TOKEN;
+    const bool quantize_here = is_hp(a_dtype);
+    if (!quantize_here || !per_token) {
+        if (!a_scales) return FP8SG_E_NULL;  // an input in these modes
+    }
+    if ((a && !aligned(a, 16)) || (wq && !aligned(wq, 16)) || !aligned(y, 16)) return FP8SG_E_ALIGN;
+    if ((a_scales && !aligned(a_scales, 4)) || !aligned(w_scales, 4)) return FP8SG_E_ALIGN;
+    const size_t need = fp8_scaled_gemm_workspace_size(a_dtype, a_scale_mode, M, N, K);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return FP8SG_E_WORKSPACE;
+        if (!aligned(workspace, 256)) return FP8SG_E_ALIGN;
+    }
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    hipStream_t s = (hipStream_t)stream;
+
+    const uint8_t* aq = (const uint8_t*)a;
+    const float* sa = a_scales;
+    if (quantize_here) {
+        uint8_t* ws_q = (uint8_t*)workspace;
+        hipError_t e;
+        if (per_token) {
+            float* sc = a_scales ? a_scales : (float*)((uint8_t*)workspace + align256((size_t)M * (size_t)K));
+            e = fp8sg::launch_row_quant(a, a_dtype == FP8SG_BF16, M, K, ws_q, sc, s);
+            sa = sc;
+        } else {
+            e = fp8sg::launch_grouped_quant(a, a_dtype == FP8SG_BF16, M * K, a_scales, 1, 1, 0, ws_q, s);
+        }
+        if (e != hipSuccess) return FP8SG_E_LAUNCH;
+        aq = ws_q;
+    }
+    return launched(fp8sg::launch_gemm(aq, sa, per_token, wq, w_scales, y, y_dtype == FP8SG_BF16, M, N, K,
+                                       accum == FP8SG_ACCUM_MFMA_FP8, s));
+}
+
+fp8sg_status fp8_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,
+                              float* head_scales, void* stream) {
+    int64_t numel = 0;
+    fp8sg_status st = kv_shape(B, S, H, D, fmt, &numel);
+    if (st != FP8SG_OK) return st;
+    if (H == 0) return FP8SG_OK;
+    if (!head_scales || (numel > 0 && !kv)) return FP8SG_E_NULL;
+    if ((kv && !aligned(kv, 16)) || !aligned(head_scales, 4)) return FP8SG_E_ALIGN;
+    st = device_ok();
+    if (st != FP8SG_OK) return st;
+    return launched(fp8sg::launch_kv_calibrate(kv, B, S, H, D, fmt == FP8SG_E4M3 ? 0 : 1, head_scales,
+                                               (hipStream_t)stream));
+}
+
+fp8sg_status fp8_kv_quant(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, const float* head_scales,
+                          int fmt, uint8_t* out, void* stream) {
+    int64_t numel = 0;
+    fp8sg_status st = kv_shape(B, S, H, D, fmt, &numel);
+    if (st != FP8SG_OK) return st;
+    if (numel == 0) return FP8SG_OK;
+    if (!kv || !head_scales || !out) return FP8SG_E_NULL;
+    if (!aligned(kv, 16) || !aligned(out, 16) || !aligned(head_scales, 4)) return FP8SG_E_ALIGN;
+    st = device_ok();
+    if (st != FP8SG_OK) return st;
+    return launched(fp8sg::launch_grouped_quant(kv, true, numel, head_scales, D / 16, (int)H,
+                                                fmt == FP8SG_E4M3 ? 0 : 1, out, (hipStream_t)stream));
+}
+
+fp8sg_status fp8_kv_dequant(const uint8_t* kvq, int64_t B, int64_t S, int64_t H, int64_t D, const float* head_scales,
+                            int fmt, uint16_t* out, void* stream) {
+    int64_t numel = 0;
+    fp8sg_status st = kv_shape(B, S, H, D, fmt, &numel);
+    if (st != FP8SG_OK) return st;
+    if (numel == 0) return FP8SG_OK;
+    if (!kvq || !head_scales || !out) return FP8SG_E_NULL;
+    if (!aligned(kvq, 16) || !aligned(out, 16) || !aligned(head_scales, 4)) return FP8SG_E_ALIGN;
+    st = device_ok();
+    if (st != FP8SG_OK) return st;
+    return launched(fp8sg::launch_kv_dequant(kvq, numel, H, D, head_scales, fmt == FP8SG_E4M3 ? 0 : 1, out,
+                                             (hipStream_t)stream));
+}
+
+fp8sg_status fp8_kv_append(const uint16_t* kv_new, const int32_t* pos, int64_t B, int64_t S_cap, int64_t H,
+                           int64_t D, const float* head_scales, int fmt, uint8_t* cache, void* stream) {
+    int64_t numel = 0;
+    fp8sg_status st = kv_shape(B, S_cap, H, D, fmt, &numel);
+    if (st != FP8SG_OK) return st;
+    if (B == 0 || H == 0 || D == 0) return FP8SG_OK;
+    if (!kv_new || !pos || !head_scales || (!cache && S_cap > 0)) return FP8SG_E_NULL;
+    if (!aligned(kv_new, 16) || !aligned(pos, 4) || !aligned(head_scales, 4)) return FP8SG_E_ALIGN;
+    if (cache && !aligned(cache, 16)) return FP8SG_E_ALIGN;
+    if (S_cap == 0) return FP8SG_OK;  // no position is valid
+    st = device_ok();
+    if (st != FP8SG_OK) return st;
+    return launched(fp8sg::launch_kv_append(kv_new, pos, B, S_cap, H, D, head_scales, fmt == FP8SG_E4M3 ? 0 : 1,
+                                            cache, (hipStream_t)stream));
+}
+
+}  // extern "C"

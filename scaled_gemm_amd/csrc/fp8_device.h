@@ -1,0 +1,157 @@
+// Device helpers for the gfx950 FP8 kernels: exact float32 quotient, FP8
+// packing/unpacking, bf16 conversion and reductions.
+//
+// Instruction facts these helpers rely on (checked on gfx950 against an
+// independent CPU encoder over every float32 bit pattern):
+//  * v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 round to nearest even into OCP E4M3 /
+//    E5M2 exactly for every finite |t| below the format maximum, subnormals and
+//    signed zero included.  They do NOT saturate (E4M3 turns values from 480 up
+//    into NaN) and give the negative-NaN code for every NaN input, so callers
+//    bound magnitudes first.
+//  * v_cvt_pk_f32_fp8 / v_cvt_pk_f32_bf8 and v_cvt_scalef32_pk_bf16_fp8 with
+//    scale 1.0 decode exactly; v_cvt_pk_bf16_f32 rounds to nearest even.
+//  * The compiler's float division (v_div_scale/fmas/fixup) is correctly
+//    rounded, and so is 1.0f / s.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8sg {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Everything a thread needs to turn x into RN32(x / s) without a per-element
+// division.  With r = RN32(1/s) (correctly rounded), q0 = RN(|x| r) is within
+// two units in the last place of |x| / s, and each fused correction
+// q <- RN(q + RN(|x| - q s) r) (Markstein's scheme) moves it to the correctly
+// rounded quotient; one correction is exact for bf16 inputs (8 significant
+// bits; checked exhaustively over every bf16 significand against every float32
+// significand of s), two for float32 inputs.  The scheme needs s and 1/s to be
+// normal with room to spare, so scales outside [2^-60, 2^60] fall back to the
+// hardware-exact division.
+struct QScale {
+    float s;      // the stored scale
+    float r;      // RN32(1 / s)
+    float c;      // magnitude bound: RN32(fmax * s); |x| beyond it saturates anyway
+    int fast;     // s in [2^-60, 2^60]
+};
+
+__device__ __forceinline__ QScale make_qscale(float s, float fmax) {
+    QScale p;
+    p.s = s;
+    p.r = 1.0f / s;
+    p.c = fmax * s;
+    p.fast = (s >= 0x1p-60f) && (s <= 0x1p60f);
+    return p;
+}
+
+// RN32(|x| / s) for |x| already bounded by the caller; kTwoCorrections for
+// float32 inputs.
+template <bool kTwoCorrections>
+__device__ __forceinline__ float abs_quotient(float a, const QScale& p) {
+    if (p.fast) {
+        float q = a * p.r;
+        float e = __builtin_fmaf(-q, p.s, a);
+        q = __builtin_fmaf(e, p.r, q);
+        if (kTwoCorrections) {
+            e = __builtin_fmaf(-q, p.s, a);
+            q = __builtin_fmaf(e, p.r, q);
+        }
+        return q;
+    }
+    return a / p.s;
+}
+
+// Signed quotient for the dynamic (amax-derived) path: |x| <= amax, so the
+// quotient never exceeds fmax by more than a rounding, and stays far below the
+// converter's overflow point.
+template <bool kTwoCorrections>
+__device__ __forceinline__ float quotient_dynamic(float x, const QScale& p) {
+    return __builtin_copysignf(abs_quotient<kTwoCorrections>(__builtin_fabsf(x), p), x);
+}
+
+// Signed quotient for the given-scale path: |x| is first bounded by
+// c = RN32(fmax s) with a NaN-propagating minimum; every |x| >= c encodes to
+// the maximum code, and the bounded quotient RN32(c / s) lies within a
+// rounding of fmax, so it also encodes to the maximum.  +-inf saturates, NaN
+// stays NaN.
+template <bool kTwoCorrections>
+__device__ __forceinline__ float quotient_given(float x, const QScale& p) {
+    float a = __builtin_elementwise_minimum(__builtin_fabsf(x), p.c);
+    return __builtin_copysignf(abs_quotient<kTwoCorrections>(a, p), x);
+}
+
+// Four quotients -> four codes in one dword (byte i = code of t_i).
+template <int kFmt>  // 0 = E4M3, 1 = E5M2
+__device__ __forceinline__ uint32_t pack4(float t0, float t1, float t2, float t3) {
+    int w;
+    if (kFmt == 0) {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(t0, t1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(t2, t3, w, true);
+    }
+    return (uint32_t)w;
+}
+
+// Two codes (bytes 0,1 or 2,3 of w) -> two floats, exact.
+template <int kFmt>
+__device__ __forceinline__ f32x2 unpack2(uint32_t w, bool hi) {
+    if (kFmt == 0) return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    return hi ? __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+}
+
+// Two floats -> two bf16 (round to nearest even) packed in a dword, low first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    bf16x2 h = __builtin_convertvector(v, bf16x2);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
+}
+
+// Two E4M3 codes (bytes 0,1 or 2,3 of w) -> two bf16 in a dword, exact.
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+    bf16x2 h = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Block-wide maximum of non-negative values; every thread gets the result.
+// `red` must hold one float per wave of the block.
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = (blockDim.x + 63) >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float m = red[0];
+    for (int i = 1; i < nwaves; ++i) m = fmaxf(m, red[i]);
+    __syncthreads();
+    return m;
+}
+
+// Dynamic scale rule: s = RN32(amax / fmax), 1.0 when that is 0.
+__device__ __forceinline__ float dynamic_scale(float amax, float fmax) {
+    float s = amax / fmax;
+    return s == 0.0f ? 1.0f : s;
+}
+
+}  // namespace fp8sg

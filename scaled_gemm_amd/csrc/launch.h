@@ -1,0 +1,30 @@
+// Internal launchers (host side).  Each enqueues kernels on `stream` and returns
+// hipGetLastError(); arguments are already validated by the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8sg {
+
+hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
+                            hipStream_t stream);
+
+hipError_t launch_grouped_quant(const void* x, bool x_is_bf16, int64_t numel, const float* scales,
+                                int64_t inner_units, int nscales, int fmt, uint8_t* q, hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* aq, const float* a_scales, bool a_per_token, const uint8_t* wq,
+                       const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
+                       bool fp8_mfma, hipStream_t stream);
+
+hipError_t launch_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,
+                               float* head_scales, hipStream_t stream);
+
+hipError_t launch_kv_dequant(const uint8_t* kvq, int64_t numel, int64_t H, int64_t D, const float* head_scales,
+                             int fmt, uint16_t* out, hipStream_t stream);
+
+hipError_t launch_kv_append(const uint16_t* kv_new, const int32_t* pos, int64_t B, int64_t S_cap, int64_t H,
+                            int64_t D, const float* head_scales, int fmt, uint8_t* cache, hipStream_t stream);
+
+}  // namespace fp8sg

@@ -1,0 +1,227 @@
+// FP8 quantizer kernels for gfx950.
+//
+//  * row_quant: dynamic per-row scaling (per-token activations, per-output-
+//    channel weights).  One workgroup per row; the row stays in registers
+//    between the absolute-maximum reduction and the encode, so X is read from
+//    HBM once (FP8 Inference Explained, in depth -- "Inside a quantized linear
+//    layer": find each token's amax, divide, cast to E4M3).
+//  * grouped_quant: given scales, one per group of `inner` consecutive
+//    elements, cycling over `nscales` groups (static per-tensor: one group;
+//    KV cache [B,S,H,D]: inner = D, nscales = H).  Saturating (Quantization: FP8
+//    inference and KV-cache quantization -- "Dynamic scales or static scales").
+//
+// Memory access: 16-byte loads and stores, consecutive lanes on consecutive
+// 16-byte chunks; both kernels are bound by HBM bandwidth.
+#include "fp8_device.h"
+#include "launch.h"
+
+namespace fp8sg {
+
+// ---------------------------------------------------------------------------
+// Row-wise dynamic quantization.
+// A chunk is 8 consecutive elements: one 16-byte load for bf16, two for fp32.
+template <typename InT>
+__device__ __forceinline__ void load_chunk(const InT* p, float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load_chunk<uint16_t>(const uint16_t* p, float (&v)[8]) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+    v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+    v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+}
+
+template <>
+__device__ __forceinline__ void load_chunk<float>(const float* p, float (&v)[8]) {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename InT>
+__device__ __forceinline__ uint2 encode_chunk_dynamic(const float (&v)[8], const QScale& p) {
+    constexpr bool kTwo = sizeof(InT) == 4;
+    uint2 o;
+    o.x = pack4<0>(quotient_dynamic<kTwo>(v[0], p), quotient_dynamic<kTwo>(v[1], p),
+                   quotient_dynamic<kTwo>(v[2], p), quotient_dynamic<kTwo>(v[3], p));
+    o.y = pack4<0>(quotient_dynamic<kTwo>(v[4], p), quotient_dynamic<kTwo>(v[5], p),
+                   quotient_dynamic<kTwo>(v[6], p), quotient_dynamic<kTwo>(v[7], p));
+    return o;
+}
+
+// kChunks chunks per thread held in registers (row length <= kChunks * 8 * blockDim).
+template <typename InT, int kChunks>
+__global__ __launch_bounds__(256) void row_quant_resident(const InT* __restrict__ x, int64_t K,
+                                                          uint8_t* __restrict__ q, float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const InT* xr = x + row * K;
+    uint8_t* qr = q + row * K;
+    const int nchunks = (int)(K >> 3);
+    const int T = blockDim.x;
+    float v[kChunks][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int c = threadIdx.x + i * T;
+        if (c < nchunks) {
+            load_chunk<InT>(xr + (int64_t)c * 8, v[i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(v[i][j]));
+        }
+    }
+    amax = block_max(amax, red);
+    const float s = dynamic_scale(amax, kE4M3Max);
+    if (threadIdx.x == 0) scales[row] = s;
+    const QScale p = make_qscale(s, kE4M3Max);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int c = threadIdx.x + i * T;
+        if (c < nchunks) *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) = encode_chunk_dynamic<InT>(v[i], p);
+    }
+}
+
+// Rows too long for registers: the maximum pass and the encode pass each read the row.
+template <typename InT>
+__global__ __launch_bounds__(256) void row_quant_stream(const InT* __restrict__ x, int64_t K,
+                                                        uint8_t* __restrict__ q, float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const InT* xr = x + row * K;
+    uint8_t* qr = q + row * K;
+    const int64_t nchunks = K >> 3;
+    float amax = 0.0f;
+    for (int64_t c = threadIdx.x; c < nchunks; c += blockDim.x) {
+        float v[8];
+        load_chunk<InT>(xr + c * 8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
+    }
+    amax = block_max(amax, red);
+    const float s = dynamic_scale(amax, kE4M3Max);
+    if (threadIdx.x == 0) scales[row] = s;
+    const QScale p = make_qscale(s, kE4M3Max);
+    for (int64_t c = threadIdx.x; c < nchunks; c += blockDim.x) {
+        float v[8];
+        load_chunk<InT>(xr + c * 8, v);
+        *reinterpret_cast<uint2*>(qr + c * 8) = encode_chunk_dynamic<InT>(v, p);
+    }
+}
+
+template <typename InT>
+static hipError_t launch_row_quant_t(const InT* x, int64_t M, int64_t K, uint8_t* q, float* scales,
+                                     hipStream_t stream) {
+    const int64_t nchunks = K / 8;
+    int T = (int)((nchunks + 63) / 64 * 64);
+    if (T > 256) T = 256;
+    if (T < 64) T = 64;
+    const int64_t per = (nchunks + T - 1) / T;
+    dim3 grid((unsigned)M), block(T);
+    if (per <= 1) row_quant_resident<InT, 1><<<grid, block, 0, stream>>>(x, K, q, scales);
+    else if (per <= 2) row_quant_resident<InT, 2><<<grid, block, 0, stream>>>(x, K, q, scales);
+    else if (per <= 4) row_quant_resident<InT, 4><<<grid, block, 0, stream>>>(x, K, q, scales);
+    else if (per <= 8) row_quant_resident<InT, 8><<<grid, block, 0, stream>>>(x, K, q, scales);
+    else row_quant_stream<InT><<<grid, block, 0, stream>>>(x, K, q, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
+                            hipStream_t stream) {
+    if (M == 0) return hipSuccess;
+    if (x_is_bf16) return launch_row_quant_t<uint16_t>((const uint16_t*)x, M, K, q, scales, stream);
+    return launch_row_quant_t<float>((const float*)x, M, K, q, scales, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Given-scale quantization, one scale per group of `inner` elements cycling
+// over `nscales` scales.  A unit is 16 consecutive elements -> 16 codes (one
+// 16-byte store).  The caller passes inner_units = inner / 16 (inner is a
+// multiple of 16 whenever nscales > 1), so a unit never straddles two scales;
+// with nscales == 1 every unit uses scale 0.  When the grid stride is a
+// multiple of the scale period (inner_units * nscales units) a thread's scale
+// never changes and is looked up once.  A partial last unit (numel % 16) takes a
+// per-element path.
+constexpr int kMaxLdsScales = 256;
+
+template <typename InT, int kFmt>
+__device__ __forceinline__ uint4 encode16_given(const InT* p, const QScale& sc) {
+    constexpr bool kTwo = sizeof(InT) == 4;
+    float v[8], w[8];
+    load_chunk<InT>(p, v);
+    load_chunk<InT>(p + 8, w);
+    uint4 o;
+    o.x = pack4<kFmt>(quotient_given<kTwo>(v[0], sc), quotient_given<kTwo>(v[1], sc),
+                      quotient_given<kTwo>(v[2], sc), quotient_given<kTwo>(v[3], sc));
+    o.y = pack4<kFmt>(quotient_given<kTwo>(v[4], sc), quotient_given<kTwo>(v[5], sc),
+                      quotient_given<kTwo>(v[6], sc), quotient_given<kTwo>(v[7], sc));
+    o.z = pack4<kFmt>(quotient_given<kTwo>(w[0], sc), quotient_given<kTwo>(w[1], sc),
+                      quotient_given<kTwo>(w[2], sc), quotient_given<kTwo>(w[3], sc));
+    o.w = pack4<kFmt>(quotient_given<kTwo>(w[4], sc), quotient_given<kTwo>(w[5], sc),
+                      quotient_given<kTwo>(w[6], sc), quotient_given<kTwo>(w[7], sc));
+    return o;
+}
+
+template <typename InT, int kFmt>
+__global__ __launch_bounds__(256) void grouped_quant(const InT* __restrict__ x, int64_t numel,
+                                                     const float* __restrict__ scales, int64_t inner_units,
+                                                     int nscales, uint8_t* __restrict__ q) {
+    constexpr bool kTwo = sizeof(InT) == 4;
+    constexpr float fmax = kFmt == 0 ? kE4M3Max : kE5M2Max;
+    __shared__ QScale tab[kMaxLdsScales];
+    const bool in_lds = nscales <= kMaxLdsScales;
+    if (in_lds) {
+        for (int i = threadIdx.x; i < nscales; i += blockDim.x) tab[i] = make_qscale(scales[i], fmax);
+        __syncthreads();
+    }
+    const int64_t nfull = numel >> 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t period = inner_units * nscales;
+    int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (stride % period == 0) {
+        const int g = (int)((u / inner_units) % nscales);
+        const QScale p = in_lds ? tab[g] : make_qscale(scales[g], fmax);
+        for (; u < nfull; u += stride)
+            *reinterpret_cast<uint4*>(q + (u << 4)) = encode16_given<InT, kFmt>(x + (u << 4), p);
+    } else {
+        for (; u < nfull; u += stride) {
+            const int g = (int)((u / inner_units) % nscales);
+            const QScale p = in_lds ? tab[g] : make_qscale(scales[g], fmax);
+            *reinterpret_cast<uint4*>(q + (u << 4)) = encode16_given<InT, kFmt>(x + (u << 4), p);
+        }
+    }
+    // tail: the last numel % 16 elements, one thread
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        for (int64_t e = nfull << 4; e < numel; ++e) {
+            const int g = (int)(((e >> 4) / inner_units) % nscales);
+            const QScale p = in_lds ? tab[g] : make_qscale(scales[g], fmax);
+            float xv;
+            if (sizeof(InT) == 2) xv = bf16_lo((uint32_t)((const uint16_t*)x)[e]);
+            else xv = ((const float*)x)[e];
+            q[e] = (uint8_t)(pack4<kFmt>(quotient_given<kTwo>(xv, p), 0.0f, 0.0f, 0.0f) & 0xFFu);
+        }
+    }
+}
+
+hipError_t launch_grouped_quant(const void* x, bool x_is_bf16, int64_t numel, const float* scales,
+                                int64_t inner_units, int nscales, int fmt, uint8_t* q, hipStream_t stream) {
+    if (numel == 0) return hipSuccess;
+    const int64_t nunits = (numel + 15) / 16;
+    const int T = 256;
+    int64_t blocks = (nunits + T - 1) / T;
+    const int64_t cap = 256 * 16;  // resident waves enough to saturate HBM; the loop strides the rest
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    dim3 grid((unsigned)blocks), block(T);
+    if (x_is_bf16) {
+        if (fmt == 0) grouped_quant<uint16_t, 0><<<grid, block, 0, stream>>>((const uint16_t*)x, numel, scales, inner_units, nscales, q);
+        else grouped_quant<uint16_t, 1><<<grid, block, 0, stream>>>((const uint16_t*)x, numel, scales, inner_units, nscales, q);
+    } else {
+        if (fmt == 0) grouped_quant<float, 0><<<grid, block, 0, stream>>>((const float*)x, numel, scales, inner_units, nscales, q);
+        else grouped_quant<float, 1><<<grid, block, 0, stream>>>((const float*)x, numel, scales, inner_units, nscales, q);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fp8sg

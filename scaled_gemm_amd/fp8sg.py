@@ -1,0 +1,258 @@
+"""Thin Python binding of libfp8sg (include/fp8sg.h) for torch tensors.
+
+Argument marshalling only: each function checks devices, dtypes and
+contiguity, allocates outputs with torch when the caller does not pass them,
+and calls the C entry point of the same name on the current HIP stream.  All
+arithmetic happens in the library's HIP kernels.  If the library is not built
+the import of a function fails loudly (there is no fallback path).
+
+FP8 codes travel as torch.uint8 tensors; bf16 data as torch.bfloat16.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libfp8sg.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8sg.h")
+
+# enums of include/fp8sg.h
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_DEVICE, E_LAUNCH, E_WORKSPACE = range(8)
+F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
+SCALE_PER_TOKEN, SCALE_PER_TENSOR = 0, 1
+ACCUM_EXACT, ACCUM_MFMA_FP8 = 0, 1
+
+_FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+_ACCUM = {"exact": ACCUM_EXACT, "mfma_fp8": ACCUM_MFMA_FP8, ACCUM_EXACT: ACCUM_EXACT,
+          ACCUM_MFMA_FP8: ACCUM_MFMA_FP8}
+_SCALE = {"per_token": SCALE_PER_TOKEN, "per_tensor": SCALE_PER_TENSOR, SCALE_PER_TOKEN: SCALE_PER_TOKEN,
+          SCALE_PER_TENSOR: SCALE_PER_TENSOR}
+
+
+class Fp8sgError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+_SIGS = {
+    "fp8sg_status_string": (ctypes.c_char_p, [_i32]),
+    "fp8sg_version": (_i32, []),
+    "fp8_quant_per_token": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_quant_per_tensor_static": (_i32, [_vp, _i32, _i64, _vp, _i32, _vp, _vp]),
+    "fp8_quant_weight_per_channel": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_scaled_gemm_workspace_size": (_sz, [_i32, _i32, _i64, _i64, _i64]),
+    "fp8_scaled_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "fp8_kv_calibrate": (_i32, [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "fp8_kv_quant": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
+    "fp8_kv_dequant": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
+    "fp8_kv_append": (_i32, [_vp, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
+}
+
+
+def lib():
+    """The loaded library with argument types set; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libfp8sg is not built ({LIB_PATH} missing): run `python -m scaled_gemm_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def declared_symbols(header: str = HEADER_PATH):
+    """Function names declared in include/fp8sg.h."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8\w*)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().fp8sg_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise Fp8sgError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _hp_code(t: torch.Tensor) -> int:
+    return BF16 if t.dtype == torch.bfloat16 else F32
+
+
+_HP = (torch.float32, torch.bfloat16)
+
+
+def fp8_quant_per_token(x: torch.Tensor, q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """x [M, K] (bf16/fp32) -> (q [M, K] uint8 E4M3, scales [M] fp32)."""
+    _need(x, "x", _HP)
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty((M,), dtype=torch.float32, device=x.device) if scales is None else scales
+    _need(q, "q", (torch.uint8,), (M, K))
+    _need(scales, "scales", (torch.float32,), (M,))
+    _check(lib().fp8_quant_per_token(_ptr(x), _hp_code(x), M, K, _ptr(q), _ptr(scales), _stream(stream)),
+           "fp8_quant_per_token")
+    return q, scales
+
+
+def fp8_quant_weight_per_channel(w: torch.Tensor, wq: Optional[torch.Tensor] = None,
+                                 w_scales: Optional[torch.Tensor] = None, stream=None):
+    """w [N, K] (fp32/bf16) -> (wq [N, K] uint8 E4M3, w_scales [N] fp32)."""
+    _need(w, "w", _HP)
+    N, K = w.shape
+    wq = torch.empty((N, K), dtype=torch.uint8, device=w.device) if wq is None else wq
+    w_scales = torch.empty((N,), dtype=torch.float32, device=w.device) if w_scales is None else w_scales
+    _need(wq, "wq", (torch.uint8,), (N, K))
+    _need(w_scales, "w_scales", (torch.float32,), (N,))
+    _check(lib().fp8_quant_weight_per_channel(_ptr(w), _hp_code(w), N, K, _ptr(wq), _ptr(w_scales),
+                                              _stream(stream)), "fp8_quant_weight_per_channel")
+    return wq, w_scales
+
+
+def fp8_quant_per_tensor_static(x: torch.Tensor, scale: torch.Tensor, fmt="e4m3", q: Optional[torch.Tensor] = None,
+                                stream=None) -> torch.Tensor:
+    """x (bf16/fp32, any shape) with a device scale [1] -> codes uint8 of x's shape."""
+    _need(x, "x", _HP)
+    _need(scale, "scale", (torch.float32,), (1,))
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    _need(q, "q", (torch.uint8,), tuple(x.shape))
+    _check(lib().fp8_quant_per_tensor_static(_ptr(x), _hp_code(x), x.numel(), _ptr(scale), _FMT[fmt], _ptr(q),
+                                             _stream(stream)), "fp8_quant_per_tensor_static")
+    return q
+
+
+def fp8_scaled_gemm_workspace_size(a_dtype, a_scale_mode, M: int, N: int, K: int) -> int:
+    code = {torch.uint8: E4M3, torch.bfloat16: BF16, torch.float32: F32}.get(a_dtype, a_dtype)
+    return int(lib().fp8_scaled_gemm_workspace_size(code, _SCALE[a_scale_mode], M, N, K))
+
+
+def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor, w_scales: torch.Tensor, *,
+                    a_scale_mode="per_token", out_dtype=torch.bfloat16, accum="exact",
+                    y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Y [M, N] = diag(s_a) (A_q W_q^T) diag(s_w).
+
+    a: uint8 E4M3 codes [M, K] (a_scales is then an input), or bf16/fp32
+    activations that the call quantizes first (per token: a_scales, if given,
+    receives the computed scales; per tensor: a_scales [1] is the given scale).
+    """
+    _need(a, "a", (torch.uint8, torch.bfloat16, torch.float32))
+    _need(wq, "wq", (torch.uint8,))
+    M, K = a.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError(f"wq has K={wq.shape[1]}, a has K={K}")
+    _need(w_scales, "w_scales", (torch.float32,), (N,))
+    mode = _SCALE[a_scale_mode]
+    if a_scales is not None:
+        _need(a_scales, "a_scales", (torch.float32,), (M,) if mode == SCALE_PER_TOKEN else (1,))
+    a_code = {torch.uint8: E4M3, torch.bfloat16: BF16, torch.float32: F32}[a.dtype]
+    y_code = {torch.bfloat16: BF16, torch.float32: F32}[out_dtype]
+    y = torch.empty((M, N), dtype=out_dtype, device=a.device) if y is None else y
+    _need(y, "y", (out_dtype,), (M, N))
+    need = int(lib().fp8_scaled_gemm_workspace_size(a_code, mode, M, N, K))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8_scaled_gemm(_ptr(a), a_code, _ptr(a_scales), mode, _ptr(wq), _ptr(w_scales), _ptr(y), y_code,
+                                 M, N, K, _ACCUM[accum], _ptr(workspace), ws_bytes, _stream(stream)),
+           "fp8_scaled_gemm")
+    return y
+
+
+def _kv_dims(t: torch.Tensor):
+    if t.dim() != 4:
+        raise ValueError("KV tensors are [B, S, H, D]")
+    return tuple(int(v) for v in t.shape)
+
+
+def fp8_kv_calibrate(kv: torch.Tensor, fmt="e4m3", head_scales: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """kv [B, S, H, D] bf16 -> head_scales [H] fp32."""
+    _need(kv, "kv", (torch.bfloat16,))
+    B, S, H, D = _kv_dims(kv)
+    head_scales = torch.empty((H,), dtype=torch.float32, device=kv.device) if head_scales is None else head_scales
+    _need(head_scales, "head_scales", (torch.float32,), (H,))
+    _check(lib().fp8_kv_calibrate(_ptr(kv), B, S, H, D, _FMT[fmt], _ptr(head_scales), _stream(stream)),
+           "fp8_kv_calibrate")
+    return head_scales
+
+
+def fp8_kv_quant(kv: torch.Tensor, head_scales: torch.Tensor, fmt="e4m3", out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """kv [B, S, H, D] bf16 -> codes uint8 [B, S, H, D]."""
+    _need(kv, "kv", (torch.bfloat16,))
+    B, S, H, D = _kv_dims(kv)
+    _need(head_scales, "head_scales", (torch.float32,), (H,))
+    out = torch.empty(kv.shape, dtype=torch.uint8, device=kv.device) if out is None else out
+    _need(out, "out", (torch.uint8,), tuple(kv.shape))
+    _check(lib().fp8_kv_quant(_ptr(kv), B, S, H, D, _ptr(head_scales), _FMT[fmt], _ptr(out), _stream(stream)),
+           "fp8_kv_quant")
+    return out
+
+
+def fp8_kv_dequant(kvq: torch.Tensor, head_scales: torch.Tensor, fmt="e4m3", out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """codes uint8 [B, S, H, D] -> bf16 [B, S, H, D]."""
+    _need(kvq, "kvq", (torch.uint8,))
+    B, S, H, D = _kv_dims(kvq)
+    _need(head_scales, "head_scales", (torch.float32,), (H,))
+    out = torch.empty(kvq.shape, dtype=torch.bfloat16, device=kvq.device) if out is None else out
+    _need(out, "out", (torch.bfloat16,), tuple(kvq.shape))
+    _check(lib().fp8_kv_dequant(_ptr(kvq), B, S, H, D, _ptr(head_scales), _FMT[fmt], _ptr(out), _stream(stream)),
+           "fp8_kv_dequant")
+    return out
+
+
+def fp8_kv_append(kv_new: torch.Tensor, pos: torch.Tensor, head_scales: torch.Tensor, cache: torch.Tensor,
+                  fmt="e4m3", stream=None) -> torch.Tensor:
+    """kv_new [B, H, D] bf16, pos [B] int32, cache [B, S_cap, H, D] uint8 (updated in place)."""
+    _need(kv_new, "kv_new", (torch.bfloat16,))
+    _need(cache, "cache", (torch.uint8,))
+    B, S_cap, H, D = _kv_dims(cache)
+    if tuple(kv_new.shape) != (B, H, D):
+        raise ValueError(f"kv_new has shape {tuple(kv_new.shape)}, expected {(B, H, D)}")
+    _need(pos, "pos", (torch.int32,), (B,))
+    _need(head_scales, "head_scales", (torch.float32,), (H,))
+    _check(lib().fp8_kv_append(_ptr(kv_new), _ptr(pos), B, S_cap, H, D, _ptr(head_scales), _FMT[fmt], _ptr(cache),
+                               _stream(stream)), "fp8_kv_append")
+    return cache

@@ -1,0 +1,124 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/fp8sg.h declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import scaled_gemm_amd as sg
+from scaled_gemm_amd import fp8sg as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = sg.declared_symbols()
+    assert len(names) == 11
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = sg.lib()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings_and_version():
+    assert sg.lib().fp8sg_version() == 1
+    for st in range(8):
+        assert sg.status_string(st)
+    assert sg.status_string(99) == "unknown status"
+
+
+def test_binding_names_match_the_header():
+    py = {n for n in dir(sg) if n.startswith("fp8_")}
+    declared = {n for n in sg.declared_symbols() if n.startswith("fp8_")}
+    assert declared <= py
+
+
+L = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sg.lib()
+
+
+A = 4096  # a 16-byte-aligned fake device address: never dereferenced, validation fails first
+
+
+def test_quant_validation(lib):
+    assert lib.fp8_quant_per_token(A, 7, 4, 16, A, A, None) == b.E_DTYPE
+    assert lib.fp8_quant_per_token(A, b.BF16, 4, 17, A, A, None) == b.E_SHAPE
+    assert lib.fp8_quant_per_token(A, b.BF16, -1, 16, A, A, None) == b.E_SHAPE
+    assert lib.fp8_quant_per_token(None, b.BF16, 4, 16, A, A, None) == b.E_NULL
+    assert lib.fp8_quant_per_token(A, b.BF16, 4, 16, A, None, None) == b.E_NULL
+    assert lib.fp8_quant_per_token(A + 8, b.BF16, 4, 16, A, A, None) == b.E_ALIGN
+    assert lib.fp8_quant_per_token(A, b.BF16, 4, 16, A, A + 2, None) == b.E_ALIGN
+    assert lib.fp8_quant_per_token(A, b.BF16, 0, 16, None, None, None) == b.OK
+    assert lib.fp8_quant_weight_per_channel(A, b.E4M3, 4, 16, A, A, None) == b.E_DTYPE
+    assert lib.fp8_quant_per_tensor_static(A, b.F32, 100, A, 9, A, None) == b.E_DTYPE
+    assert lib.fp8_quant_per_tensor_static(A, b.E4M3, 100, A, b.E4M3, A, None) == b.E_DTYPE
+    assert lib.fp8_quant_per_tensor_static(A, b.F32, 100, None, b.E4M3, A, None) == b.E_NULL
+    assert lib.fp8_quant_per_tensor_static(A, b.F32, 0, None, b.E4M3, None, None) == b.OK
+
+
+def test_gemm_validation(lib):
+    g = lib.fp8_scaled_gemm
+    ok = dict(a=A, a_dt=b.E4M3, sa=A, mode=b.SCALE_PER_TOKEN, wq=A, sw=A, y=A, y_dt=b.BF16, M=4, N=8, K=128,
+              accum=b.ACCUM_EXACT, ws=None, wsb=0)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return g(d["a"], d["a_dt"], d["sa"], d["mode"], d["wq"], d["sw"], d["y"], d["y_dt"], d["M"], d["N"], d["K"],
+                 d["accum"], d["ws"], d["wsb"], None)
+
+    assert call(K=100) == b.E_SHAPE
+    assert call(a_dt=b.E5M2) == b.E_DTYPE
+    assert call(y_dt=b.E4M3) == b.E_DTYPE
+    assert call(mode=5) == b.E_DTYPE
+    assert call(accum=2) == b.E_DTYPE
+    assert call(sa=None) == b.E_NULL
+    assert call(wq=None) == b.E_NULL
+    assert call(y=A + 4) == b.E_ALIGN
+    assert call(M=0) == b.OK
+    # a bf16 activation needs the workspace the size query reports
+    need = lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4, 8, 128)
+    assert need == 512 + 256
+    assert lib.fp8_scaled_gemm_workspace_size(b.E4M3, b.SCALE_PER_TOKEN, 4, 8, 128) == 0
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TENSOR, 4, 8, 128) == 512
+    assert call(a_dt=b.BF16, sa=None) == b.E_WORKSPACE
+    assert call(a_dt=b.BF16, sa=None, ws=A, wsb=need - 1) == b.E_WORKSPACE
+    assert call(a_dt=b.BF16, sa=None, ws=A + 16, wsb=need) == b.E_ALIGN
+    assert call(a_dt=b.BF16, mode=b.SCALE_PER_TENSOR, sa=None, ws=A, wsb=need) == b.E_NULL
+
+
+def test_kv_validation(lib):
+    assert lib.fp8_kv_quant(A, 2, 4, 8, 24, A, b.E4M3, A, None) == b.E_SHAPE
+    assert lib.fp8_kv_quant(A, 2, 4, 8, 32, A, b.BF16, A, None) == b.E_DTYPE
+    assert lib.fp8_kv_quant(None, 2, 4, 8, 32, A, b.E4M3, A, None) == b.E_NULL
+    assert lib.fp8_kv_dequant(A, 2, 4, 8, 32, None, b.E5M2, A, None) == b.E_NULL
+    assert lib.fp8_kv_dequant(A + 1, 2, 4, 8, 32, A, b.E5M2, A, None) == b.E_ALIGN
+    assert lib.fp8_kv_calibrate(A, 2, 4, 8, 32, b.E4M3, None, None) == b.E_NULL
+    assert lib.fp8_kv_append(A, None, 2, 4, 8, 32, A, b.E4M3, A, None) == b.E_NULL
+    assert lib.fp8_kv_append(A, A + 2, 2, 4, 8, 32, A, b.E4M3, A, None) == b.E_ALIGN
+    assert lib.fp8_kv_quant(A, 0, 4, 8, 32, A, b.E4M3, A, None) == b.OK
+
+
+def test_no_device_is_reported_not_faked(lib):
+    """Valid arguments on a machine without a gfx950 device: FP8SG_E_DEVICE, never
+    a silent fallback."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a HIP device is present")
+    assert lib.fp8_quant_per_token(A, b.BF16, 4, 16, A, A, None) == b.E_DEVICE
+    assert lib.fp8_kv_quant(A, 2, 4, 8, 32, A, b.E4M3, A, None) == b.E_DEVICE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        sg.fp8_quant_per_token(torch.zeros((2, 16), dtype=torch.bfloat16))
