@@ -1,0 +1,407 @@
+"""Benchmark of the FP8 W8A8 scaled-GEMM path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--workload NAME ...]
+
+Prints ONE JSON line.  The headline step is the decode-shaped W8A8 GEMM:
+for M in (1, 8, 32), one fp8_scaled_gemm call on bf16 activations X [M, 4096]
+(per-token dynamic E4M3 quantization fused into the call) against E4M3 weights
+[14336, 4096] with per-channel scales, exact fp32 accumulation, bf16 output.
+`value` is that step's algorithmic HBM traffic divided by its time (GB/s):
+weights + weight scales + X (bf16) + Y (bf16) per call, inputs resident in HBM.
+The weights rotate through enough copies (8 x 58.7 MB) that the 256 MB
+last-level cache cannot serve them.
+
+`roofline` is for the step's dominant kernel, the skinny GEMM of the M = 32
+call, timed per launch with HIP events on the library's stream (pre-quantized
+activations, so the GEMM kernel is the only kernel between the events).
+`cpu_baseline` times the CPU oracle on the same decode workload.
+`details` carries every other measured workload (prefill and large-layer GEMMs
+in both accumulation modes, the quantizers, the KV-cache passes).
+
+Inputs are seeded and synthetic (see workloads/).  One GPU only: --gpus > 1
+exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp8_scaled_gemm TFLOPS + quant GB/s at 1 MI355X, as % of MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # dense FP8 matrix cores
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
+DEC_N, DEC_K = 14336, 4096
+DEC_MS = (1, 8, 32)
+W_COPIES = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--quick", action="store_true", help="headline only: skip the detail workloads")
+    ap.add_argument("--workload", nargs="*", default=None,
+                    help="detail workloads to run (default all): prefill large quant kv weights")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import scaled_gemm_amd as sg
+    from workloads import decode_inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no HIP device"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    def to_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def timed_events(fn, iters, warmup):
+        """Per-call HIP-event durations (ms) of fn(i), all on the current stream."""
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for i in range(iters):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    # ------------------------------------------------------------ headline inputs
+    log("generating decode inputs")
+    w_host = None
+    xs = {}
+    for m in DEC_MS:
+        xb, w, _ = decode_inputs(m, with_weight=(w_host is None))
+        if w_host is None:
+            w_host = w
+        xs[m] = to_bf16(xb)
+    w_t = torch.from_numpy(w_host).to(dev)
+    wq0, sw = sg.fp8_quant_weight_per_channel(w_t)
+    del w_t
+    wqs = [wq0] + [wq0.clone() for _ in range(W_COPIES - 1)]
+    ys = {m: torch.empty((m, DEC_N), dtype=torch.bfloat16, device=dev) for m in DEC_MS}
+    ws = {m: torch.empty(sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", m, DEC_N, DEC_K),
+                         dtype=torch.uint8, device=dev) for m in DEC_MS}
+    sas = {m: torch.empty(m, dtype=torch.float32, device=dev) for m in DEC_MS}
+    torch.cuda.synchronize()
+
+    def step(i):
+        wq = wqs[i % W_COPIES]
+        for m in DEC_MS:
+            sg.fp8_scaled_gemm(xs[m], sas[m], wq, sw, y=ys[m], workspace=ws[m])
+
+    # ------------------------------------------------------------ headline timing
+    log(f"headline: warmup {args.warmup}, steps {args.steps}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    bytes_per_call = {m: DEC_N * DEC_K + 4 * DEC_N + 2 * m * DEC_K + 2 * m * DEC_N for m in DEC_MS}
+    step_bytes = sum(bytes_per_call.values())
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ------------------------------------------------------------ dominant kernel
+    details = []
+    kern = {}
+    for m in DEC_MS:
+        aq, sa = sg.fp8_quant_per_token(xs[m])
+        for accum in ("exact", "mfma_fp8"):
+            d = timed_events(lambda i: sg.fp8_scaled_gemm(aq, sa, wqs[i % W_COPIES], sw, y=ys[m], accum=accum),
+                             200, 20)
+            # algorithmic bytes of the GEMM kernel alone: W + s_w + A_q + s_a + Y
+            kb = DEC_N * DEC_K + 4 * DEC_N + m * DEC_K + 4 * m + 2 * m * DEC_N
+            kern[(m, accum)] = (kb, float(d.mean()))
+            details.append({"workload": f"decode GEMM kernel M={m} N={DEC_N} K={DEC_K} (pre-quantized A)",
+                            "accum": accum, "avg_us": round(float(d.mean()) * 1e3, 2),
+                            "median_us": round(float(np.median(d)) * 1e3, 2),
+                            "GB_s": round(kb / (d.mean() * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(kb / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        d = timed_events(lambda i: sg.fp8_scaled_gemm(xs[m], sas[m], wqs[i % W_COPIES], sw, y=ys[m],
+                                                      workspace=ws[m]), 200, 20)
+        details.append({"workload": f"decode call M={m} (fused per-token quant + GEMM)", "accum": "exact",
+                        "avg_us": round(float(d.mean()) * 1e3, 2),
+                        "GB_s": round(bytes_per_call[m] / (d.mean() * 1e-3) / 1e9, 1)})
+    kb32, dur32 = kern[(32, "exact")]
+    achieved = kb32 / (dur32 * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemm_skinny<exact, bf16 out, 2 m-tiles> (decode M=32)",
+                "avg_launch_us": round(dur32 * 1e3, 2), "bytes_per_launch": kb32}
+
+    # ------------------------------------------------------------ details
+    wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights"}
+    if args.quick:
+        wanted = set()
+    del wqs[1:]
+    torch.cuda.empty_cache()
+    if wanted:
+        details += run_details(sg, torch, dev, to_bf16, timed_events, wanted, log)
+
+    # ------------------------------------------------------------ copy calibration
+    if args.pmc_calibrate:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        details.append({"workload": "calibration copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                        "launches": 3})
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w_host, log)
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "e4m3", "data": "synthetic (seeded, workloads/)",
+           "config": {"workload": "decode-shaped W8A8 GEMM: X bf16 [M,4096] M in {1,8,32}, per-token dynamic E4M3 "
+                                  "quant fused into the call; W E4M3 [14336,4096] per-channel fp32 scales; exact fp32 "
+                                  "accumulation; bf16 out",
+                      "M": list(DEC_MS), "N": DEC_N, "K": DEC_K, "accum": "exact", "weight_copies": W_COPIES,
+                      "bytes_per_step": step_bytes},
+           "roofline": roofline, "cpu_baseline": cpu, "details": details}
+    print(json.dumps(out), flush=True)
+
+
+def _gbs(nbytes, ms):
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def _tflops(flops, ms):
+    return round(flops / (ms * 1e-3) / 1e12, 1)
+
+
+def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
+    """Every other configuration: prefill and large-layer GEMMs (both accumulation
+    modes), per-token / static / per-channel quantizers and the KV-cache passes."""
+    from workloads import (STATIC_SCALE_DEN, STATIC_SCALE_NUM, kv_append_inputs, kv_inputs, large_layer_inputs,
+                           prefill_inputs)
+    out = []
+
+    def copies(t, n):
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    def gemm_rows(tag, x_list, wq, sw, M, N, K, static_scale=None):
+        flops = 2.0 * M * N * K
+        if static_scale is None:
+            aq, sa = sg.fp8_quant_per_token(x_list[0])
+        else:
+            sa = torch.tensor([static_scale], dtype=torch.float32, device=dev)
+            aq = sg.fp8_quant_per_tensor_static(x_list[0], sa)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for accum in ("exact", "mfma_fp8"):
+            d = timed_events(lambda i: sg.fp8_scaled_gemm(aq, sa, wq, sw, y=y, accum=accum,
+                                                          a_scale_mode="per_token" if static_scale is None
+                                                          else "per_tensor"), 20, 3)
+            tf = _tflops(flops, d.mean())
+            row = {"workload": f"{tag} GEMM {M}x{N}x{K} (pre-quantized A)", "accum": accum,
+                   "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
+                   "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+            if accum == "exact":
+                row["frac_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
+            out.append(row)
+        ws = torch.empty(sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", M, N, K), dtype=torch.uint8,
+                         device=dev)
+        mode = "per_token" if static_scale is None else "per_tensor"
+        sa_in = None if static_scale is None else sa
+        d = timed_events(lambda i: sg.fp8_scaled_gemm(x_list[i % len(x_list)], sa_in, wq, sw, y=y, workspace=ws,
+                                                      a_scale_mode=mode), 20, 3)
+        out.append({"workload": f"{tag} call {M}x{N}x{K} (bf16 X, {mode} quant fused)", "accum": "exact",
+                    "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": _tflops(flops, d.mean())})
+        return aq, sa
+
+    def quant_rows(tag, x_list, M, K, static_scale=None):
+        nbytes = 3 * M * K + (4 * M if static_scale is None else 4)
+        q = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in x_list]
+        if static_scale is None:
+            s = [torch.empty(M, dtype=torch.float32, device=dev) for _ in x_list]
+            d = timed_events(lambda i: sg.fp8_quant_per_token(x_list[i % len(x_list)], q[i % len(q)],
+                                                              s[i % len(s)]), 50, 5)
+            name = "per-token dynamic quant"
+        else:
+            sc = torch.tensor([static_scale], dtype=torch.float32, device=dev)
+            d = timed_events(lambda i: sg.fp8_quant_per_tensor_static(x_list[i % len(x_list)], sc,
+                                                                      q=q[i % len(q)]), 50, 5)
+            name = "per-tensor static quant"
+        gbs = _gbs(nbytes, d.mean())
+        out.append({"workload": f"{tag} {name} X bf16 [{M},{K}]", "avg_us": round(float(d.mean()) * 1e3, 2),
+                    "GB_s": gbs, "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "buffers": len(x_list)})
+
+    if "prefill" in wanted or "quant" in wanted:
+        for K in (4096, 14336):
+            log(f"prefill K={K}")
+            xb, w, _ = prefill_inputs(K)
+            M, N = xb.shape[0], w.shape[0]
+            x0 = to_bf16(xb)
+            xl = copies(x0, 4 if K == 4096 else 2)
+            if "quant" in wanted:
+                quant_rows(f"prefill K={K}", xl, M, K)
+            if "prefill" in wanted:
+                wq, sw = sg.fp8_quant_weight_per_channel(torch.from_numpy(w).to(dev))
+                gemm_rows(f"prefill K={K}", xl, wq, sw, M, N, K)
+                del wq, sw
+            del xl, x0
+            torch.cuda.empty_cache()
+
+    if "large" in wanted or "quant" in wanted:
+        log("large layer")
+        xb, w = large_layer_inputs()
+        M, K = xb.shape
+        N = w.shape[0]
+        s_static = float(np.float32(STATIC_SCALE_NUM) / np.float32(STATIC_SCALE_DEN))
+        x0 = to_bf16(xb)
+        xl = copies(x0, 4)
+        if "quant" in wanted:
+            quant_rows("large-layer", xl, M, K, static_scale=s_static)
+            quant_rows("large-layer", xl, M, K)
+        if "large" in wanted:
+            w_t = torch.from_numpy(w).to(dev)
+            wq, sw = sg.fp8_quant_weight_per_channel(w_t)
+            aq_s, sa_s = gemm_rows("large-layer static", xl, wq, sw, M, N, K, static_scale=s_static)
+            aq_d, sa_d = gemm_rows("large-layer dynamic", xl, wq, sw, M, N, K)
+            # static vs dynamic on the same seed: saturated codes, and relative Frobenius error of Y
+            # against the float64 product of the unquantized X and W, on 256 rows
+            sat_static = int(((aq_s & 0x7F) == 0x7E).sum())
+            sat_dyn = int(((aq_d & 0x7F) == 0x7E).sum())
+            rows = torch.arange(0, M, M // 256, device=dev)[:256]
+            ref = x0[rows].double() @ w_t.double().t()
+            rel = {}
+            for tag, aq, sa, mode in (("static", aq_s, sa_s, "per_tensor"), ("dynamic", aq_d, sa_d, "per_token")):
+                y = sg.fp8_scaled_gemm(aq, sa, wq, sw, a_scale_mode=mode)
+                rel[tag] = float((y[rows].double() - ref).norm() / ref.norm())
+            n_big = int((x0.float().abs() * float(1.0 / s_static) >= 448.0).sum())
+            out.append({"workload": "large-layer static vs dynamic (same seed)", "static_scale": s_static,
+                        "codes_at_max_static": sat_static, "codes_at_max_dynamic": sat_dyn,
+                        "inputs_beyond_448s_static": n_big, "rel_frobenius_static": round(rel["static"], 6),
+                        "rel_frobenius_dynamic": round(rel["dynamic"], 6), "rows_compared": 256})
+            del w_t, wq, sw, ref
+        del xl, x0
+        torch.cuda.empty_cache()
+
+    if "weights" in wanted:
+        log("weight quant")
+        from workloads import decode_inputs
+        _, w, _ = decode_inputs(1)
+        w_t = torch.from_numpy(w).to(dev)
+        N, K = w.shape
+        d = timed_events(lambda i: sg.fp8_quant_weight_per_channel(w_t), 20, 3)
+        out.append({"workload": f"per-channel weight quant W fp32 [{N},{K}] (offline)",
+                    "avg_us": round(float(d.mean()) * 1e3, 1), "GB_s": _gbs(5 * N * K + 4 * N, d.mean()),
+                    "frac_hbm": round(_gbs(5 * N * K + 4 * N, d.mean()) / HBM_PEAK_GBS, 4)})
+        del w_t
+
+    if "kv" in wanted:
+        log("kv cache")
+        k, v, kc, vc = kv_inputs(0)
+        B, S, H, D = k.shape
+        numel = B * S * H * D
+        kt, vt = to_bf16(k), to_bf16(v)
+        del k, v
+        for fmt in ("e4m3", "e5m2"):
+            sk = sg.fp8_kv_calibrate(kt, fmt)
+            sv = sg.fp8_kv_calibrate(vt, fmt)
+            qk = sg.fp8_kv_quant(kt, sk, fmt)
+            qv = sg.fp8_kv_quant(vt, sv, fmt)
+            dk = torch.empty_like(kt)
+            dv = torch.empty_like(vt)
+            d = timed_events(lambda i: (sg.fp8_kv_calibrate(kt, fmt, sk), sg.fp8_kv_calibrate(vt, fmt, sv)), 10, 2)
+            out.append({"workload": f"KV calibrate K+V [{B},{S},{H},{D}] {fmt}", "avg_us": round(float(d.mean()) * 1e3, 1),
+                        "GB_s": _gbs(4 * numel, d.mean()), "frac_hbm": round(_gbs(4 * numel, d.mean()) / HBM_PEAK_GBS, 4)})
+            d = timed_events(lambda i: (sg.fp8_kv_quant(kt, sk, fmt, out=qk), sg.fp8_kv_quant(vt, sv, fmt, out=qv)),
+                             10, 2)
+            out.append({"workload": f"KV quant K+V [{B},{S},{H},{D}] {fmt}", "avg_us": round(float(d.mean()) * 1e3, 1),
+                        "GB_s": _gbs(6 * numel, d.mean()), "frac_hbm": round(_gbs(6 * numel, d.mean()) / HBM_PEAK_GBS, 4)})
+            d = timed_events(lambda i: (sg.fp8_kv_dequant(qk, sk, fmt, out=dk), sg.fp8_kv_dequant(qv, sv, fmt, out=dv)),
+                             10, 2)
+            out.append({"workload": f"KV dequant K+V [{B},{S},{H},{D}] {fmt}", "avg_us": round(float(d.mean()) * 1e3, 1),
+                        "GB_s": _gbs(6 * numel, d.mean()), "frac_hbm": round(_gbs(6 * numel, d.mean()) / HBM_PEAK_GBS, 4)})
+            del qk, qv, dk, dv
+        kn, vn = kv_append_inputs(kc, vc)
+        knt, vnt = to_bf16(kn), to_bf16(vn)
+        del kt, vt
+        torch.cuda.empty_cache()
+        ck = torch.zeros((B, S + 1, H, D), dtype=torch.uint8, device=dev)
+        cv = torch.zeros_like(ck)
+        pos = torch.full((B,), S, dtype=torch.int32, device=dev)
+        d = timed_events(lambda i: (sg.fp8_kv_append(knt, pos, sk, ck, "e5m2"), sg.fp8_kv_append(vnt, pos, sv, cv, "e5m2")),
+                         200, 20)
+        out.append({"workload": f"KV append 1 token/seq K+V into [{B},{S + 1},{H},{D}]", "avg_us": round(float(d.mean()) * 1e3, 2),
+                    "bytes": 2 * (B * H * D * 3)})
+        del ck, cv
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w_host, log):
+    """The CPU oracle on the decode workload: per-token quantization of X plus the
+    exact GEMM and bf16 epilogue, for M = 1, 8, 32 (the weight quantization is the
+    offline step and is not timed).  Reported in the headline unit (GB/s of the
+    same algorithmic bytes)."""
+    from oracle import w8a8
+    from workloads import decode_inputs, f32_from_bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    log("cpu baseline: oracle weight quantization (untimed)")
+    # a bounded sample: the first 4096 of the 14336 output channels
+    nsub = 4096
+    wq, sw = w8a8.quant_weight_per_channel(w_host[:nsub])
+    xs = {m: f32_from_bf16_bits(decode_inputs(m, with_weight=False)[0]) for m in DEC_MS}
+    t = time.perf_counter()
+    reps = 0
+    while True:
+        for m in DEC_MS:
+            aq, sa = w8a8.quant_per_token(xs[m])
+            w8a8.scaled_gemm_bf16(aq, sa, wq, sw)
+        reps += 1
+        if time.perf_counter() - t > 10.0 or reps >= 20:
+            break
+    dt = (time.perf_counter() - t) / reps
+    sample_bytes = sum(nsub * DEC_K + 4 * nsub + 2 * m * DEC_K + 2 * m * nsub for m in DEC_MS)
+    return {"value": round(sample_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"decode step (M=1,8,32, K=4096) on 4096 of the 14336 weight rows, {reps} reps, "
+                      f"{dt * 1e3:.1f} ms per step; numpy/BLAS on {os.cpu_count()} host CPUs "
+                      f"(BLAS threads {blas_threads}, the encoder single-threaded)"}
+
+
+if __name__ == "__main__":
+    main()
