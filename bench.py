@@ -81,18 +81,25 @@ def main():
     def to_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def timed_events(fn, iters, warmup):
-        """Per-call HIP-event durations (ms) of fn(i), all on the current stream."""
+    def timed_events(fn, iters, warmup, reps=5):
+        """Average duration (ms) of fn(i), from HIP events on the current stream
+        (the stream the library launches on) around `iters` back-to-back calls;
+        `reps` such measurements are returned.  Back-to-back launches keep the
+        queue full, so the average is the kernels' own duration plus the small
+        dispatch gap between them -- the figure a kernel trace reports."""
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-        for i in range(iters):
-            ev[i][0].record()
-            fn(i)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        return np.array([a.elapsed_time(b) for a, b in ev])
+        out = []
+        for r in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(iters):
+                fn(r * iters + i)
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / iters)
+        return np.array(out)
 
     # ------------------------------------------------------------ headline inputs
     log("generating decode inputs")
@@ -104,9 +111,13 @@ def main():
             w_host = w
         xs[m] = to_bf16(xb)
     w_t = torch.from_numpy(w_host).to(dev)
-    wq0, sw = sg.fp8_quant_weight_per_channel(w_t)
+    wq_rm, sw = sg.fp8_quant_weight_per_channel(w_t)
     del w_t
-    wqs = [wq0] + [wq0.clone() for _ in range(W_COPIES - 1)]
+    # weights are prepared offline: quantized per channel, then packed into the
+    # matrix-core fragment order; W_COPIES copies defeat the last-level cache
+    wp0 = sg.fp8_pack_weights(wq_rm)
+    wqs = [wp0] + [wp0.clone() for _ in range(W_COPIES - 1)]
+    wrm = [wq_rm] + [wq_rm.clone() for _ in range(W_COPIES - 1)]
     ys = {m: torch.empty((m, DEC_N), dtype=torch.bfloat16, device=dev) for m in DEC_MS}
     ws = {m: torch.empty(sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", m, DEC_N, DEC_K),
                          dtype=torch.uint8, device=dev) for m in DEC_MS}
@@ -116,7 +127,7 @@ def main():
     def step(i):
         wq = wqs[i % W_COPIES]
         for m in DEC_MS:
-            sg.fp8_scaled_gemm(xs[m], sas[m], wq, sw, y=ys[m], workspace=ws[m])
+            sg.fp8_scaled_gemm(xs[m], sas[m], wq, sw, y=ys[m], workspace=ws[m], w_layout="packed")
 
     # ------------------------------------------------------------ headline timing
     log(f"headline: warmup {args.warmup}, steps {args.steps}")
@@ -141,34 +152,36 @@ def main():
     kern = {}
     for m in DEC_MS:
         aq, sa = sg.fp8_quant_per_token(xs[m])
-        for accum in ("exact", "mfma_fp8"):
-            d = timed_events(lambda i: sg.fp8_scaled_gemm(aq, sa, wqs[i % W_COPIES], sw, y=ys[m], accum=accum),
-                             200, 20)
-            # algorithmic bytes of the GEMM kernel alone: W + s_w + A_q + s_a + Y
-            kb = DEC_N * DEC_K + 4 * DEC_N + m * DEC_K + 4 * m + 2 * m * DEC_N
-            kern[(m, accum)] = (kb, float(d.mean()))
-            details.append({"workload": f"decode GEMM kernel M={m} N={DEC_N} K={DEC_K} (pre-quantized A)",
-                            "accum": accum, "avg_us": round(float(d.mean()) * 1e3, 2),
-                            "median_us": round(float(np.median(d)) * 1e3, 2),
-                            "GB_s": round(kb / (d.mean() * 1e-3) / 1e9, 1),
-                            "frac_hbm": round(kb / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        for layout, bufs in (("packed", wqs), ("row_major", wrm)):
+            for accum in ("exact", "mfma_fp8"):
+                d = timed_events(lambda i: sg.fp8_scaled_gemm(aq, sa, bufs[i % W_COPIES], sw, y=ys[m], accum=accum,
+                                                              w_layout=layout), 100, 20)
+                # algorithmic bytes of the GEMM kernel alone: W + s_w + A_q + s_a + Y
+                kb = DEC_N * DEC_K + 4 * DEC_N + m * DEC_K + 4 * m + 2 * m * DEC_N
+                kern[(m, accum, layout)] = (kb, float(d.mean()))
+                details.append({"workload": f"decode GEMM kernel M={m} N={DEC_N} K={DEC_K} (pre-quantized A)",
+                                "accum": accum, "w_layout": layout, "avg_us": round(float(d.mean()) * 1e3, 2),
+                                "min_us": round(float(np.min(d)) * 1e3, 2),
+                                "GB_s": round(kb / (d.mean() * 1e-3) / 1e9, 1),
+                                "frac_hbm": round(kb / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         d = timed_events(lambda i: sg.fp8_scaled_gemm(xs[m], sas[m], wqs[i % W_COPIES], sw, y=ys[m],
-                                                      workspace=ws[m]), 200, 20)
+                                                      workspace=ws[m], w_layout="packed"), 100, 20)
         details.append({"workload": f"decode call M={m} (fused per-token quant + GEMM)", "accum": "exact",
-                        "avg_us": round(float(d.mean()) * 1e3, 2),
+                        "w_layout": "packed", "avg_us": round(float(d.mean()) * 1e3, 2),
                         "GB_s": round(bytes_per_call[m] / (d.mean() * 1e-3) / 1e9, 1)})
-    kb32, dur32 = kern[(32, "exact")]
+    kb32, dur32 = kern[(32, "exact", "packed")]
     achieved = kb32 / (dur32 * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemm_skinny<exact, bf16 out, 2 m-tiles> (decode M=32)",
-                "avg_launch_us": round(dur32 * 1e3, 2), "bytes_per_launch": kb32}
+                "kernel": "gemm_skinny<exact, bf16 out, 2 m-tiles, packed W> (decode M=32)",
+                "avg_launch_us": round(dur32 * 1e3, 2), "bytes_per_launch": kb32,
+                "timing": "HIP events around 100 back-to-back launches on the library's stream, mean of 5"}
 
     # ------------------------------------------------------------ details
     wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights"}
     if args.quick:
         wanted = set()
-    del wqs[1:]
+    del wqs[1:], wrm[1:]
     torch.cuda.empty_cache()
     if wanted:
         details += run_details(sg, torch, dev, to_bf16, timed_events, wanted, log)
@@ -192,9 +205,10 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "e4m3", "data": "synthetic (seeded, workloads/)",
            "config": {"workload": "decode-shaped W8A8 GEMM: X bf16 [M,4096] M in {1,8,32}, per-token dynamic E4M3 "
-                                  "quant fused into the call; W E4M3 [14336,4096] per-channel fp32 scales; exact fp32 "
-                                  "accumulation; bf16 out",
-                      "M": list(DEC_MS), "N": DEC_N, "K": DEC_K, "accum": "exact", "weight_copies": W_COPIES,
+                                  "quant fused into the call; W E4M3 [14336,4096] per-channel fp32 scales, packed "
+                                  "offline; exact fp32 accumulation; bf16 out",
+                      "M": list(DEC_MS), "N": DEC_N, "K": DEC_K, "accum": "exact", "w_layout": "packed",
+                      "weight_copies": W_COPIES,
                       "bytes_per_step": step_bytes},
            "roofline": roofline, "cpu_baseline": cpu, "details": details}
     print(json.dumps(out), flush=True)
@@ -218,20 +232,21 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
     def copies(t, n):
         return [t] + [t.clone() for _ in range(n - 1)]
 
-    def gemm_rows(tag, x_list, wq, sw, M, N, K, static_scale=None):
+    def gemm_rows(tag, x_list, wq_rm, sw, M, N, K, static_scale=None):
         flops = 2.0 * M * N * K
+        wq = sg.fp8_pack_weights(wq_rm)
         if static_scale is None:
             aq, sa = sg.fp8_quant_per_token(x_list[0])
         else:
             sa = torch.tensor([static_scale], dtype=torch.float32, device=dev)
             aq = sg.fp8_quant_per_tensor_static(x_list[0], sa)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        for accum in ("exact", "mfma_fp8"):
-            d = timed_events(lambda i: sg.fp8_scaled_gemm(aq, sa, wq, sw, y=y, accum=accum,
+        for accum, layout, wbuf in (("exact", "packed", wq), ("mfma_fp8", "packed", wq), ("exact", "row_major", wq_rm)):
+            d = timed_events(lambda i: sg.fp8_scaled_gemm(aq, sa, wbuf, sw, y=y, accum=accum, w_layout=layout,
                                                           a_scale_mode="per_token" if static_scale is None
-                                                          else "per_tensor"), 20, 3)
+                                                          else "per_tensor"), 10, 3, reps=3)
             tf = _tflops(flops, d.mean())
-            row = {"workload": f"{tag} GEMM {M}x{N}x{K} (pre-quantized A)", "accum": accum,
+            row = {"workload": f"{tag} GEMM {M}x{N}x{K} (pre-quantized A)", "accum": accum, "w_layout": layout,
                    "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
                    "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
             if accum == "exact":
@@ -242,7 +257,7 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
         mode = "per_token" if static_scale is None else "per_tensor"
         sa_in = None if static_scale is None else sa
         d = timed_events(lambda i: sg.fp8_scaled_gemm(x_list[i % len(x_list)], sa_in, wq, sw, y=y, workspace=ws,
-                                                      a_scale_mode=mode), 20, 3)
+                                                      a_scale_mode=mode, w_layout="packed"), 10, 3, reps=3)
         out.append({"workload": f"{tag} call {M}x{N}x{K} (bf16 X, {mode} quant fused)", "accum": "exact",
                     "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": _tflops(flops, d.mean())})
         return aq, sa
@@ -253,12 +268,12 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
         if static_scale is None:
             s = [torch.empty(M, dtype=torch.float32, device=dev) for _ in x_list]
             d = timed_events(lambda i: sg.fp8_quant_per_token(x_list[i % len(x_list)], q[i % len(q)],
-                                                              s[i % len(s)]), 50, 5)
+                                                              s[i % len(s)]), 50, 5, reps=3)
             name = "per-token dynamic quant"
         else:
             sc = torch.tensor([static_scale], dtype=torch.float32, device=dev)
             d = timed_events(lambda i: sg.fp8_quant_per_tensor_static(x_list[i % len(x_list)], sc,
-                                                                      q=q[i % len(q)]), 50, 5)
+                                                                      q=q[i % len(q)]), 50, 5, reps=3)
             name = "per-tensor static quant"
         gbs = _gbs(nbytes, d.mean())
         out.append({"workload": f"{tag} {name} X bf16 [{M},{K}]", "avg_us": round(float(d.mean()) * 1e3, 2),
@@ -304,7 +319,7 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
             ref = x0[rows].double() @ w_t.double().t()
             rel = {}
             for tag, aq, sa, mode in (("static", aq_s, sa_s, "per_tensor"), ("dynamic", aq_d, sa_d, "per_token")):
-                y = sg.fp8_scaled_gemm(aq, sa, wq, sw, a_scale_mode=mode)
+                y = sg.fp8_scaled_gemm(aq, sa, wq, sw, a_scale_mode=mode)  # row-major W
                 rel[tag] = float((y[rows].double() - ref).norm() / ref.norm())
             n_big = int((x0.float().abs() * float(1.0 / s_static) >= 448.0).sum())
             out.append({"workload": "large-layer static vs dynamic (same seed)", "static_scale": s_static,
@@ -321,7 +336,7 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
         _, w, _ = decode_inputs(1)
         w_t = torch.from_numpy(w).to(dev)
         N, K = w.shape
-        d = timed_events(lambda i: sg.fp8_quant_weight_per_channel(w_t), 20, 3)
+        d = timed_events(lambda i: sg.fp8_quant_weight_per_channel(w_t), 20, 3, reps=3)
         out.append({"workload": f"per-channel weight quant W fp32 [{N},{K}] (offline)",
                     "avg_us": round(float(d.mean()) * 1e3, 1), "GB_s": _gbs(5 * N * K + 4 * N, d.mean()),
                     "frac_hbm": round(_gbs(5 * N * K + 4 * N, d.mean()) / HBM_PEAK_GBS, 4)})
@@ -341,15 +356,15 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
             qv = sg.fp8_kv_quant(vt, sv, fmt)
             dk = torch.empty_like(kt)
             dv = torch.empty_like(vt)
-            d = timed_events(lambda i: (sg.fp8_kv_calibrate(kt, fmt, sk), sg.fp8_kv_calibrate(vt, fmt, sv)), 10, 2)
+            d = timed_events(lambda i: (sg.fp8_kv_calibrate(kt, fmt, sk), sg.fp8_kv_calibrate(vt, fmt, sv)), 10, 2, reps=3)
             out.append({"workload": f"KV calibrate K+V [{B},{S},{H},{D}] {fmt}", "avg_us": round(float(d.mean()) * 1e3, 1),
                         "GB_s": _gbs(4 * numel, d.mean()), "frac_hbm": round(_gbs(4 * numel, d.mean()) / HBM_PEAK_GBS, 4)})
             d = timed_events(lambda i: (sg.fp8_kv_quant(kt, sk, fmt, out=qk), sg.fp8_kv_quant(vt, sv, fmt, out=qv)),
-                             10, 2)
+                             10, 2, reps=3)
             out.append({"workload": f"KV quant K+V [{B},{S},{H},{D}] {fmt}", "avg_us": round(float(d.mean()) * 1e3, 1),
                         "GB_s": _gbs(6 * numel, d.mean()), "frac_hbm": round(_gbs(6 * numel, d.mean()) / HBM_PEAK_GBS, 4)})
             d = timed_events(lambda i: (sg.fp8_kv_dequant(qk, sk, fmt, out=dk), sg.fp8_kv_dequant(qv, sv, fmt, out=dv)),
-                             10, 2)
+                             10, 2, reps=3)
             out.append({"workload": f"KV dequant K+V [{B},{S},{H},{D}] {fmt}", "avg_us": round(float(d.mean()) * 1e3, 1),
                         "GB_s": _gbs(6 * numel, d.mean()), "frac_hbm": round(_gbs(6 * numel, d.mean()) / HBM_PEAK_GBS, 4)})
             del qk, qv, dk, dv
@@ -361,7 +376,7 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
         cv = torch.zeros_like(ck)
         pos = torch.full((B,), S, dtype=torch.int32, device=dev)
         d = timed_events(lambda i: (sg.fp8_kv_append(knt, pos, sk, ck, "e5m2"), sg.fp8_kv_append(vnt, pos, sv, cv, "e5m2")),
-                         200, 20)
+                         200, 20, reps=3)
         out.append({"workload": f"KV append 1 token/seq K+V into [{B},{S + 1},{H},{D}]", "avg_us": round(float(d.mean()) * 1e3, 2),
                     "bytes": 2 * (B * H * D * 3)})
         del ck, cv

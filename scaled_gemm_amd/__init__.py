@@ -15,11 +15,15 @@ from .fp8sg import (  # noqa: F401
     Fp8sgError,
     SCALE_PER_TENSOR,
     SCALE_PER_TOKEN,
+    W_PACKED,
+    W_ROW_MAJOR,
     declared_symbols,
     fp8_kv_append,
     fp8_kv_calibrate,
     fp8_kv_dequant,
     fp8_kv_quant,
+    fp8_pack_weights,
+    fp8_packed_weight_bytes,
     fp8_quant_per_tensor_static,
     fp8_quant_per_token,
     fp8_quant_weight_per_channel,

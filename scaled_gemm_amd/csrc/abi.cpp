@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -125,13 +125,29 @@ size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, 
     return bytes;
 }
 
+size_t fp8_packed_weight_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return 0;
+    return (size_t)((N + 15) / 16 * 16) * (size_t)K;
+}
+
+fp8sg_status fp8_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, void* stream) {
+    if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim || K % 128 != 0) return FP8SG_E_SHAPE;
+    if (N == 0 || K == 0) return FP8SG_OK;
+    if (!wq || !wp) return FP8SG_E_NULL;
+    if (!aligned(wq, 16) || !aligned(wp, 16)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    return launched(fp8sg::launch_pack_weights(wq, N, K, wp, (hipStream_t)stream));
+}
+
 fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
-                             const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K, int accum,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             int w_layout, const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                             int accum, void* workspace, size_t workspace_bytes, void* stream) {
     if (!(a_dtype == FP8SG_E4M3 || is_hp(a_dtype))) return FP8SG_E_DTYPE;
     if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
     if (!(a_scale_mode == FP8SG_SCALE_PER_TOKEN || a_scale_mode == FP8SG_SCALE_PER_TENSOR)) return FP8SG_E_DTYPE;
     if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
+    if (!(w_layout == FP8SG_W_ROW_MAJOR || w_layout == FP8SG_W_PACKED)) return FP8SG_E_DTYPE;
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
     if (K % 128 != 0) return FP8SG_E_SHAPE;
     if (M == 0 || N == 0) return FP8SG_OK;
@@ -168,8 +184,8 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
         if (e != hipSuccess) return FP8SG_E_LAUNCH;
         aq = ws_q;
     }
-    return launched(fp8sg::launch_gemm(aq, sa, per_token, wq, w_scales, y, y_dtype == FP8SG_BF16, M, N, K,
-                                       accum == FP8SG_ACCUM_MFMA_FP8, s));
+    return launched(fp8sg::launch_gemm(aq, sa, per_token, wq, w_layout == FP8SG_W_PACKED, w_scales, y,
+                                       y_dtype == FP8SG_BF16, M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, s));
 }
 
 fp8sg_status fp8_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,

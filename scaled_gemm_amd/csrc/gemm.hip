@@ -24,6 +24,16 @@
 #include "fp8_device.h"
 #include "launch.h"
 
+#ifndef SKINNY_NS
+#define SKINNY_NS 2
+#endif
+#ifndef SKINNY_KS
+#define SKINNY_KS 4
+#endif
+#ifndef SKINNY_DEPTH
+#define SKINNY_DEPTH 2
+#endif
+
 namespace fp8sg {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -76,6 +86,17 @@ __device__ __forceinline__ Frag load_frag_global(const uint8_t* p) {
     return f;
 }
 
+// Packed weights: the 2048-byte block of 16-row tile t and k block kb holds the
+// 64 lanes' first 16-byte halves, then their second halves, in lane order.
+constexpr int64_t kPackBlock = 2048;
+
+__device__ __forceinline__ Frag load_frag_packed(const uint8_t* block, int lane) {
+    Frag f;
+    f.lo = reinterpret_cast<const uint4*>(block)[lane];
+    f.hi = reinterpret_cast<const uint4*>(block + 1024)[lane];
+    return f;
+}
+
 // Epilogue for one 16x16 fragment: lane holds acc[r] = C[n0 + r][m], r = 0..3.
 template <bool kYbf16>
 __device__ __forceinline__ void store4(void* y, int64_t N, int64_t m, int64_t n0, f32x4 acc, float sa,
@@ -109,39 +130,47 @@ __device__ __forceinline__ void store4(void* y, int64_t N, int64_t m, int64_t n0
 
 // ---------------------------------------------------------------------------
 // Skinny GEMM (M <= 16 * kMT), the decode shape: every byte of W is used once,
-// so W streams from HBM straight into registers.  A workgroup owns 32 rows of W
-// (two 16-row subtiles); its 4 waves split the k blocks round-robin and keep
-// kDepth k blocks of loads in flight each.  The four partial sums are added in a
-// fixed order through LDS, so the result does not depend on timing.
-template <bool kFp8, bool kYbf16, int kMT>
-__global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
-                                                   int sa_per_token, const uint8_t* __restrict__ W,
-                                                   const float* __restrict__ sw, void* __restrict__ Y, int M,
-                                                   int N, int K) {
-    constexpr int kNS = 2;      // 16-row W subtiles per workgroup
-    constexpr int kWaves = 4;
-    constexpr int kDepth = 4;   // k blocks in flight per wave
-    __shared__ f32x4 red[kWaves - 1][kNS * kMT][64];
+// so W streams from HBM straight into registers.  A workgroup owns kNS 16-row
+// subtiles of W; its kKS waves split the k blocks round-robin (wave w takes
+// blocks w, w + kKS, ...).  Each wave issues the loads of kDepth of its blocks
+// back to back, then multiplies them, so kDepth * (kNS + kMT) * 32 bytes per lane
+// are in flight; the loop body has no branches around loads (rows past M or N
+// are clamped to the last valid row and masked in the epilogue), which lets
+// the compiler wait for each block's loads separately.  The kKS partial sums
+// are added in a fixed order through LDS, so the result does not depend on
+// timing.
+template <bool kFp8, bool kYbf16, int kMT, int kNS, int kKS, int kDepth, bool kWPacked>
+__global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
+                                                        int sa_per_token, const uint8_t* __restrict__ W,
+                                                        const float* __restrict__ sw, void* __restrict__ Y, int M,
+                                                        int N, int K) {
+    __shared__ f32x4 red[kKS > 1 ? kKS - 1 : 1][kNS * kMT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n_base = (int64_t)blockIdx.x * (16 * kNS);
     const int nkb = K >> 7;
     const int r16 = lane & 15, kofs = (lane >> 4) * 32;
 
+    // row-major: this lane's row of each subtile; packed: the subtile's first block
     const uint8_t* wrow[kNS];
-    bool wok[kNS];
+    const int64_t last_tile = ((int64_t)N + 15) / 16 - 1;
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
-        const int64_t n = n_base + 16 * s + r16;
-        wok[s] = n < N;
-        wrow[s] = W + (wok[s] ? n : 0) * (int64_t)K + kofs;
+        if (kWPacked) {
+            int64_t t = (n_base >> 4) + s;
+            t = t < last_tile ? t : last_tile;
+            wrow[s] = W + t * nkb * kPackBlock;
+        } else {
+            int64_t n = n_base + 16 * s + r16;
+            n = n < N ? n : N - 1;
+            wrow[s] = W + n * (int64_t)K + kofs;
+        }
     }
     const uint8_t* arow[kMT];
-    bool aok[kMT];
 #pragma unroll
     for (int t = 0; t < kMT; ++t) {
-        const int m = 16 * t + r16;
-        aok[t] = m < M;
-        arow[t] = A + (aok[t] ? m : 0) * (int64_t)K + kofs;
+        int m = 16 * t + r16;
+        m = m < M ? m : M - 1;
+        arow[t] = A + (int64_t)m * K + kofs;
     }
 
     f32x4 acc[kNS][kMT];
@@ -150,40 +179,42 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
 #pragma unroll
         for (int t = 0; t < kMT; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    Frag wf[kDepth][kNS], af[kDepth][kMT];
-    auto issue = [&](int slot, int kb) {
-        const int64_t off = (int64_t)kb << 7;
-#pragma unroll
-        for (int s = 0; s < kNS; ++s) wf[slot][s] = wok[s] ? load_frag_global(wrow[s] + off) : zero_frag();
-#pragma unroll
-        for (int t = 0; t < kMT; ++t) af[slot][t] = aok[t] ? load_frag_global(arow[t] + off) : zero_frag();
-    };
-    // this wave's k blocks: wave, wave + 4, wave + 8, ...
-    const int my_blocks = nkb > wave ? (nkb - wave + kWaves - 1) / kWaves : 0;
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d)
-        if (d < my_blocks) issue(d, wave + d * kWaves);
-    for (int i = 0; i < my_blocks; i += kDepth) {
+    // this wave's blocks: wave + j * kKS, j < nper
+    const int nper = nkb > wave ? (nkb - wave + kKS - 1) / kKS : 0;
+    for (int j0 = 0; j0 < nper; j0 += kDepth) {
+        Frag wf[kDepth][kNS], af[kDepth][kMT];
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
-            if (i + d < my_blocks) {
+            int j = j0 + d;
+            j = j < nper ? j : nper - 1;  // a clamped (repeated) block past the end is loaded but not used
+            const int kb = wave + j * kKS;
+            const int64_t off = (int64_t)kb << 7;
+#pragma unroll
+            for (int s = 0; s < kNS; ++s)
+                wf[d][s] = kWPacked ? load_frag_packed(wrow[s] + kb * kPackBlock, lane) : load_frag_global(wrow[s] + off);
+#pragma unroll
+            for (int t = 0; t < kMT; ++t) af[d][t] = load_frag_global(arow[t] + off);
+        }
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            if (j0 + d < nper) {
 #pragma unroll
                 for (int s = 0; s < kNS; ++s)
 #pragma unroll
                     for (int t = 0; t < kMT; ++t) acc[s][t] = mma<kFp8>(wf[d][s], af[d][t], acc[s][t]);
-                const int nxt = i + d + kDepth;
-                if (nxt < my_blocks) issue(d, wave + nxt * kWaves);
             }
         }
     }
 
-    if (wave > 0) {
+    if (kKS > 1) {
+        if (wave > 0) {
 #pragma unroll
-        for (int s = 0; s < kNS; ++s)
+            for (int s = 0; s < kNS; ++s)
 #pragma unroll
-            for (int t = 0; t < kMT; ++t) red[wave - 1][s * kMT + t][lane] = acc[s][t];
+                for (int t = 0; t < kMT; ++t) red[wave - 1][s * kMT + t][lane] = acc[s][t];
+        }
+        __syncthreads();
     }
-    __syncthreads();
     if (wave == 0) {
         const bool vec_ok = (N & 3) == 0;
 #pragma unroll
@@ -192,7 +223,7 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
             for (int t = 0; t < kMT; ++t) {
                 f32x4 v = acc[s][t];
 #pragma unroll
-                for (int w = 0; w < kWaves - 1; ++w) v += red[w][s * kMT + t][lane];
+                for (int w = 0; w < kKS - 1; ++w) v += red[w][s * kMT + t][lane];
                 const int m = 16 * t + r16;
                 const int64_t n0 = n_base + 16 * s + 4 * (lane >> 4);
                 if (m < M && n0 < N) store4<kYbf16>(Y, N, m, n0, v, sa[sa_per_token ? m : 0], sw, vec_ok);
@@ -211,7 +242,7 @@ constexpr int kTile = 128;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
-template <bool kFp8, bool kYbf16>
+template <bool kFp8, bool kYbf16, bool kWPacked>
 __global__ __launch_bounds__(256, 2) void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                      int sa_per_token, const uint8_t* __restrict__ W,
                                                      const float* __restrict__ sw, void* __restrict__ Y, int M,
@@ -224,16 +255,26 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const uint8_t* __restrict__
     const int64_t m_base = (int64_t)tm * kTile, n_base = (int64_t)tn * kTile;
     const int nkb = K >> 7;
 
-    // loader: 1024 16-byte chunks per operand tile, 4 per thread
+    // loader: 1024 16-byte chunks per operand tile, 4 per thread.  A (and
+    // row-major W) go to the swizzled row layout; packed W keeps its fragment
+    // order (eight 2048-byte blocks), so its fragment reads are lane-contiguous.
+    const int64_t last_tile = ((int64_t)N + 15) / 16 - 1;
     uint4 ra[4], rw[4];
     auto gload = [&](int kb) {
         const int64_t koff = (int64_t)kb << 7;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-            const int64_t m = m_base + row, n = n_base + row;
+            const int64_t m = m_base + row;
             ra[i] = m < M ? *reinterpret_cast<const uint4*>(A + m * K + koff + c * 16) : make_uint4(0, 0, 0, 0);
-            rw[i] = n < N ? *reinterpret_cast<const uint4*>(W + n * K + koff + c * 16) : make_uint4(0, 0, 0, 0);
+            if (kWPacked) {
+                int64_t t = (n_base >> 4) + (id >> 7);
+                t = t < last_tile ? t : last_tile;
+                rw[i] = *reinterpret_cast<const uint4*>(W + (t * nkb + kb) * kPackBlock + (id & 127) * 16);
+            } else {
+                const int64_t n = n_base + row;
+                rw[i] = n < N ? *reinterpret_cast<const uint4*>(W + n * K + koff + c * 16) : make_uint4(0, 0, 0, 0);
+            }
         }
     };
     auto swrite = [&](int stage) {
@@ -241,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const uint8_t* __restrict__
         for (int i = 0; i < 4; ++i) {
             const int id = tid + 256 * i, row = id >> 3, c = id & 7;
             *reinterpret_cast<uint4*>(&lds[stage][0][swz(row, c)]) = ra[i];
-            *reinterpret_cast<uint4*>(&lds[stage][1][swz(row, c)]) = rw[i];
+            *reinterpret_cast<uint4*>(&lds[stage][1][kWPacked ? id * 16 : swz(row, c)]) = rw[i];
         }
     };
 
@@ -263,9 +304,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const uint8_t* __restrict__
         Frag wf[4], af[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int rw_ = wn * 64 + 16 * i + r16;
-            wf[i].lo = *reinterpret_cast<const uint4*>(&lds[st][1][swz(rw_, c0)]);
-            wf[i].hi = *reinterpret_cast<const uint4*>(&lds[st][1][swz(rw_, c0 + 1)]);
+            if (kWPacked) {
+                wf[i] = load_frag_packed(&lds[st][1][(wn * 4 + i) * kPackBlock], lane);
+            } else {
+                const int rw_ = wn * 64 + 16 * i + r16;
+                wf[i].lo = *reinterpret_cast<const uint4*>(&lds[st][1][swz(rw_, c0)]);
+                wf[i].hi = *reinterpret_cast<const uint4*>(&lds[st][1][swz(rw_, c0 + 1)]);
+            }
             const int ra_ = wm * 64 + 16 * i + r16;
             af[i].lo = *reinterpret_cast<const uint4*>(&lds[st][0][swz(ra_, c0)]);
             af[i].hi = *reinterpret_cast<const uint4*>(&lds[st][0][swz(ra_, c0 + 1)]);
@@ -292,34 +337,77 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const uint8_t* __restrict__
     }
 }
 
-template <bool kFp8, bool kYbf16>
+template <bool kFp8, bool kYbf16, bool kWPacked, int kMT, int kNS, int kKS, int kDepth>
+static void launch_skinny(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw, void* y,
+                          int M, int N, int K, hipStream_t stream) {
+    dim3 grid((unsigned)((N + 16 * kNS - 1) / (16 * kNS))), block(64 * kKS);
+    gemm_skinny<kFp8, kYbf16, kMT, kNS, kKS, kDepth, kWPacked>
+        <<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K);
+}
+
+template <bool kFp8, bool kYbf16, bool kWPacked>
 static hipError_t launch_gemm_t(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw,
                                 void* y, int M, int N, int K, hipStream_t stream) {
     if (M <= 16) {
-        dim3 grid((unsigned)((N + 31) / 32)), block(256);
-        gemm_skinny<kFp8, kYbf16, 1><<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K);
+        launch_skinny<kFp8, kYbf16, kWPacked, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y, M, N, K,
+                                                                                     stream);
     } else if (M <= 32) {
-        dim3 grid((unsigned)((N + 31) / 32)), block(256);
-        gemm_skinny<kFp8, kYbf16, 2><<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K);
+        launch_skinny<kFp8, kYbf16, kWPacked, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y, M, N, K,
+                                                                                     stream);
     } else {
         const int64_t tiles = (int64_t)((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
         dim3 grid((unsigned)tiles), block(256);
-        gemm_tiled<kFp8, kYbf16><<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K);
+        gemm_tiled<kFp8, kYbf16, kWPacked><<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const uint8_t* aq, const float* a_scales, bool a_per_token, const uint8_t* wq,
+template <bool kFp8, bool kWPacked>
+static hipError_t launch_gemm_y(const uint8_t* aq, const float* sa, int pt, const uint8_t* wq, const float* sw, void* y,
+                                bool y_bf16, int M, int N, int K, hipStream_t stream) {
+    return y_bf16 ? launch_gemm_t<kFp8, true, kWPacked>(aq, sa, pt, wq, sw, y, M, N, K, stream)
+                  : launch_gemm_t<kFp8, false, kWPacked>(aq, sa, pt, wq, sw, y, M, N, K, stream);
+}
+
+hipError_t launch_gemm(const uint8_t* aq, const float* a_scales, bool a_per_token, const uint8_t* wq, bool w_packed,
                        const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, bool fp8_mfma,
                        hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const int pt = a_per_token ? 1 : 0;
-    if (fp8_mfma) {
-        return y_bf16 ? launch_gemm_t<true, true>(aq, a_scales, pt, wq, w_scales, y, (int)M, (int)N, (int)K, stream)
-                      : launch_gemm_t<true, false>(aq, a_scales, pt, wq, w_scales, y, (int)M, (int)N, (int)K, stream);
-    }
-    return y_bf16 ? launch_gemm_t<false, true>(aq, a_scales, pt, wq, w_scales, y, (int)M, (int)N, (int)K, stream)
-                  : launch_gemm_t<false, false>(aq, a_scales, pt, wq, w_scales, y, (int)M, (int)N, (int)K, stream);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    if (fp8_mfma)
+        return w_packed ? launch_gemm_y<true, true>(aq, a_scales, pt, wq, w_scales, y, y_bf16, m, n, k, stream)
+                        : launch_gemm_y<true, false>(aq, a_scales, pt, wq, w_scales, y, y_bf16, m, n, k, stream);
+    return w_packed ? launch_gemm_y<false, true>(aq, a_scales, pt, wq, w_scales, y, y_bf16, m, n, k, stream)
+                    : launch_gemm_y<false, false>(aq, a_scales, pt, wq, w_scales, y, y_bf16, m, n, k, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing: one thread per 16-byte chunk of the packed buffer.  Chunk c
+// belongs to block c / 128 = (tile t, k block kb) and to half h = (c % 128) / 64
+// of lane l = c % 64, which reads row 16 t + l % 16 at byte kb * 128 + 32 (l / 16)
+// + 16 h; rows past N are written as zero codes.
+__global__ __launch_bounds__(256) void pack_weights(const uint8_t* __restrict__ wq, int64_t N, int64_t K,
+                                                    uint8_t* __restrict__ wp, int64_t nchunks) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= nchunks) return;
+    const int64_t nkb = K >> 7;
+    const int64_t block = c >> 7;
+    const int within = (int)(c & 127), h = within >> 6, l = within & 63;
+    const int64_t t = block / nkb, kb = block % nkb;
+    const int64_t row = 16 * t + (l & 15);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < N) v = *reinterpret_cast<const uint4*>(wq + row * K + kb * 128 + 32 * (l >> 4) + 16 * h);
+    reinterpret_cast<uint4*>(wp)[c] = v;
+}
+
+hipError_t launch_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, hipStream_t stream) {
+    const int64_t rows = (N + 15) / 16 * 16;
+    const int64_t nchunks = rows * K / 16;
+    if (nchunks == 0) return hipSuccess;
+    const int64_t blocks = (nchunks + 255) / 256;
+    pack_weights<<<(unsigned)blocks, 256, 0, stream>>>(wq, N, K, wp, nchunks);
+    return hipGetLastError();
 }
 
 }  // namespace fp8sg

@@ -14,9 +14,11 @@ hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K,
 hipError_t launch_grouped_quant(const void* x, bool x_is_bf16, int64_t numel, const float* scales,
                                 int64_t inner_units, int nscales, int fmt, uint8_t* q, hipStream_t stream);
 
-hipError_t launch_gemm(const uint8_t* aq, const float* a_scales, bool a_per_token, const uint8_t* wq,
+hipError_t launch_gemm(const uint8_t* aq, const float* a_scales, bool a_per_token, const uint8_t* wq, bool w_packed,
                        const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
                        bool fp8_mfma, hipStream_t stream);
+
+hipError_t launch_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, hipStream_t stream);
 
 hipError_t launch_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,
                                float* head_scales, hipStream_t stream);

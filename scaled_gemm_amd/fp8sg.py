@@ -26,11 +26,13 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8sg.h")
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_DEVICE, E_LAUNCH, E_WORKSPACE = range(8)
 F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
 SCALE_PER_TOKEN, SCALE_PER_TENSOR = 0, 1
+W_ROW_MAJOR, W_PACKED = 0, 1
 ACCUM_EXACT, ACCUM_MFMA_FP8 = 0, 1
 
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
 _ACCUM = {"exact": ACCUM_EXACT, "mfma_fp8": ACCUM_MFMA_FP8, ACCUM_EXACT: ACCUM_EXACT,
           ACCUM_MFMA_FP8: ACCUM_MFMA_FP8}
+_LAYOUT = {"row_major": W_ROW_MAJOR, "packed": W_PACKED, W_ROW_MAJOR: W_ROW_MAJOR, W_PACKED: W_PACKED}
 _SCALE = {"per_token": SCALE_PER_TOKEN, "per_tensor": SCALE_PER_TENSOR, SCALE_PER_TOKEN: SCALE_PER_TOKEN,
           SCALE_PER_TENSOR: SCALE_PER_TENSOR}
 
@@ -51,7 +53,10 @@ _SIGS = {
     "fp8_quant_per_tensor_static": (_i32, [_vp, _i32, _i64, _vp, _i32, _vp, _vp]),
     "fp8_quant_weight_per_channel": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_workspace_size": (_sz, [_i32, _i32, _i64, _i64, _i64]),
-    "fp8_scaled_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "fp8_packed_weight_bytes": (_sz, [_i64, _i64]),
+    "fp8_pack_weights": (_i32, [_vp, _i64, _i64, _vp, _vp]),
+    "fp8_scaled_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _sz,
+                               _vp]),
     "fp8_kv_calibrate": (_i32, [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp]),
     "fp8_kv_quant": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
     "fp8_kv_dequant": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
@@ -160,13 +165,28 @@ def fp8_quant_per_tensor_static(x: torch.Tensor, scale: torch.Tensor, fmt="e4m3"
     return q
 
 
+def fp8_packed_weight_bytes(N: int, K: int) -> int:
+    return int(lib().fp8_packed_weight_bytes(N, K))
+
+
+def fp8_pack_weights(wq: torch.Tensor, wp: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Row-major E4M3 codes [N, K] -> the packed fragment-order buffer (uint8, 1-D)."""
+    _need(wq, "wq", (torch.uint8,))
+    N, K = wq.shape
+    nbytes = fp8_packed_weight_bytes(N, K)
+    wp = torch.empty(nbytes, dtype=torch.uint8, device=wq.device) if wp is None else wp
+    _need(wp, "wp", (torch.uint8,), (nbytes,))
+    _check(lib().fp8_pack_weights(_ptr(wq), N, K, _ptr(wp), _stream(stream)), "fp8_pack_weights")
+    return wp
+
+
 def fp8_scaled_gemm_workspace_size(a_dtype, a_scale_mode, M: int, N: int, K: int) -> int:
     code = {torch.uint8: E4M3, torch.bfloat16: BF16, torch.float32: F32}.get(a_dtype, a_dtype)
     return int(lib().fp8_scaled_gemm_workspace_size(code, _SCALE[a_scale_mode], M, N, K))
 
 
 def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor, w_scales: torch.Tensor, *,
-                    a_scale_mode="per_token", out_dtype=torch.bfloat16, accum="exact",
+                    a_scale_mode="per_token", out_dtype=torch.bfloat16, accum="exact", w_layout="row_major",
                     y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
     """Y [M, N] = diag(s_a) (A_q W_q^T) diag(s_w).
@@ -174,14 +194,20 @@ def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch
     a: uint8 E4M3 codes [M, K] (a_scales is then an input), or bf16/fp32
     activations that the call quantizes first (per token: a_scales, if given,
     receives the computed scales; per tensor: a_scales [1] is the given scale).
+    wq: [N, K] row-major codes, or (w_layout="packed") the 1-D buffer of
+    fp8_pack_weights; N is taken from w_scales.
     """
     _need(a, "a", (torch.uint8, torch.bfloat16, torch.float32))
     _need(wq, "wq", (torch.uint8,))
+    _need(w_scales, "w_scales", (torch.float32,))
     M, K = a.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K:
-        raise ValueError(f"wq has K={wq.shape[1]}, a has K={K}")
-    _need(w_scales, "w_scales", (torch.float32,), (N,))
+    N = w_scales.shape[0]
+    layout = _LAYOUT[w_layout]
+    if layout == W_ROW_MAJOR:
+        if tuple(wq.shape) != (N, K):
+            raise ValueError(f"wq has shape {tuple(wq.shape)}, expected {(N, K)}")
+    elif wq.numel() != fp8_packed_weight_bytes(N, K):
+        raise ValueError(f"packed wq has {wq.numel()} bytes, expected {fp8_packed_weight_bytes(N, K)}")
     mode = _SCALE[a_scale_mode]
     if a_scales is not None:
         _need(a_scales, "a_scales", (torch.float32,), (M,) if mode == SCALE_PER_TOKEN else (1,))
@@ -193,8 +219,8 @@ def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().fp8_scaled_gemm(_ptr(a), a_code, _ptr(a_scales), mode, _ptr(wq), _ptr(w_scales), _ptr(y), y_code,
-                                 M, N, K, _ACCUM[accum], _ptr(workspace), ws_bytes, _stream(stream)),
+    _check(lib().fp8_scaled_gemm(_ptr(a), a_code, _ptr(a_scales), mode, _ptr(wq), layout, _ptr(w_scales), _ptr(y),
+                                 y_code, M, N, K, _ACCUM[accum], _ptr(workspace), ws_bytes, _stream(stream)),
            "fp8_scaled_gemm")
     return y
 

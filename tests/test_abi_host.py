@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     names = sg.declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
     missing = [n for n in names if n not in exported]
@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert sg.lib().fp8sg_version() == 1
+    assert sg.lib().fp8sg_version() == 2
     for st in range(8):
         assert sg.status_string(st)
     assert sg.status_string(99) == "unknown status"
@@ -67,15 +67,16 @@ def test_quant_validation(lib):
 
 def test_gemm_validation(lib):
     g = lib.fp8_scaled_gemm
-    ok = dict(a=A, a_dt=b.E4M3, sa=A, mode=b.SCALE_PER_TOKEN, wq=A, sw=A, y=A, y_dt=b.BF16, M=4, N=8, K=128,
-              accum=b.ACCUM_EXACT, ws=None, wsb=0)
+    ok = dict(a=A, a_dt=b.E4M3, sa=A, mode=b.SCALE_PER_TOKEN, wq=A, lay=b.W_ROW_MAJOR, sw=A, y=A, y_dt=b.BF16, M=4,
+              N=8, K=128, accum=b.ACCUM_EXACT, ws=None, wsb=0)
 
     def call(**kw):
         d = dict(ok)
         d.update(kw)
-        return g(d["a"], d["a_dt"], d["sa"], d["mode"], d["wq"], d["sw"], d["y"], d["y_dt"], d["M"], d["N"], d["K"],
-                 d["accum"], d["ws"], d["wsb"], None)
+        return g(d["a"], d["a_dt"], d["sa"], d["mode"], d["wq"], d["lay"], d["sw"], d["y"], d["y_dt"], d["M"], d["N"],
+                 d["K"], d["accum"], d["ws"], d["wsb"], None)
 
+    assert call(lay=2) == b.E_DTYPE
     assert call(K=100) == b.E_SHAPE
     assert call(a_dt=b.E5M2) == b.E_DTYPE
     assert call(y_dt=b.E4M3) == b.E_DTYPE
@@ -94,6 +95,47 @@ def test_gemm_validation(lib):
     assert call(a_dt=b.BF16, sa=None, ws=A, wsb=need - 1) == b.E_WORKSPACE
     assert call(a_dt=b.BF16, sa=None, ws=A + 16, wsb=need) == b.E_ALIGN
     assert call(a_dt=b.BF16, mode=b.SCALE_PER_TENSOR, sa=None, ws=A, wsb=need) == b.E_NULL
+
+
+def test_pack_validation(lib):
+    assert lib.fp8_packed_weight_bytes(17, 256) == 32 * 256
+    assert lib.fp8_packed_weight_bytes(0, 256) == 0
+    assert lib.fp8_pack_weights(A, 17, 100, A, None) == b.E_SHAPE
+    assert lib.fp8_pack_weights(None, 17, 128, A, None) == b.E_NULL
+    assert lib.fp8_pack_weights(A, 17, 128, A + 4, None) == b.E_ALIGN
+    assert lib.fp8_pack_weights(A, 0, 128, None, None) == b.OK
+
+
+def pack_reference(wq):
+    """The packed layout written out from its definition in include/fp8sg.h."""
+    import numpy as np
+    N, K = wq.shape
+    rows = (N + 15) // 16 * 16
+    w = np.zeros((rows, K), np.uint8)
+    w[:N] = wq
+    nkb = K // 128
+    out = np.zeros(rows * K, np.uint8)
+    for t in range(rows // 16):
+        for kb in range(nkb):
+            base = (t * nkb + kb) * 2048
+            for lane in range(64):
+                r = 16 * t + lane % 16
+                k0 = kb * 128 + 32 * (lane // 16)
+                out[base + lane * 16: base + lane * 16 + 16] = w[r, k0:k0 + 16]
+                out[base + 1024 + lane * 16: base + 1024 + lane * 16 + 16] = w[r, k0 + 16:k0 + 32]
+    return out
+
+
+def test_pack_reference_is_a_permutation():
+    import numpy as np
+    rng = np.random.default_rng(0)
+    wq = rng.integers(0, 256, (37, 384), dtype=np.uint8)
+    p = pack_reference(wq)
+    assert p.size == 48 * 384
+    # every original byte appears exactly once, the padding rows are zero
+    padded = np.zeros((48, 384), np.uint8)
+    padded[:37] = wq
+    assert np.array_equal(np.sort(p), np.sort(padded.ravel()))
 
 
 def test_kv_validation(lib):

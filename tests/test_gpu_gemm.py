@@ -81,7 +81,7 @@ def check_outputs(y_bits, acc_gpu, aq_rows, sa_rows, wq_rows, sw_rows, accum, wh
     assert (d[cancel] <= ulp[cancel] + 1e-5 * (absum * s_prod)[cancel]).all()
 
 
-def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""):
+def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what="", layout="row_major"):
     """Quantize W (per channel) and run the GEMM with the activation quantized
     inside the call; check W codes, activation scales and outputs on the sampled
     rows/cols against the oracle."""
@@ -94,6 +94,7 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
     cols = np.arange(N) if cols is None else np.asarray(cols)
 
     wq_t, sw_t = sg.fp8_quant_weight_per_channel(dev(w))
+    wg = sg.fp8_pack_weights(wq_t) if layout == "packed" else wq_t
     wq_ref, sw_ref = w8a8.quant_weight_per_channel(w[cols])
     wq_got = host(wq_t)[cols]
     sw_got = host(sw_t)[cols]
@@ -102,7 +103,7 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
 
     if static is None:
         sa_t = torch.empty(M, dtype=torch.float32, device="cuda")
-        y_t = sg.fp8_scaled_gemm(xt, sa_t, wq_t, sw_t, a_scale_mode="per_token", accum=accum)
+        y_t = sg.fp8_scaled_gemm(xt, sa_t, wg, sw_t, a_scale_mode="per_token", accum=accum, w_layout=layout)
         aq_ref, sa_ref = w8a8.quant_per_token(xf[rows])
         assert np.array_equal(host(sa_t)[rows].view(np.uint32), sa_ref.view(np.uint32)), f"{what}: act scales"
         # the accumulator through the same kernel: pre-quantized codes, unit scales, fp32 out
@@ -111,14 +112,14 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
     else:
         s = np.float32(static)
         sa_t = dev(np.float32([s]))
-        y_t = sg.fp8_scaled_gemm(xt, sa_t, wq_t, sw_t, a_scale_mode="per_tensor", accum=accum)
+        y_t = sg.fp8_scaled_gemm(xt, sa_t, wg, sw_t, a_scale_mode="per_tensor", accum=accum, w_layout=layout)
         aq_ref = w8a8.quant_static(xf[rows], s)
         sa_ref = np.full(len(rows), s, np.float32)
         aq_t = sg.fp8_quant_per_tensor_static(xt, sa_t)
         assert_codes_equal(host(aq_t)[rows], aq_ref, f"{what}: act codes")
     ones_m = torch.ones(M, dtype=torch.float32, device="cuda")
     ones_n = torch.ones(N, dtype=torch.float32, device="cuda")
-    acc_t = sg.fp8_scaled_gemm(aq_t, ones_m, wq_t, ones_n, out_dtype=torch.float32, accum=accum)
+    acc_t = sg.fp8_scaled_gemm(aq_t, ones_m, wg, ones_n, out_dtype=torch.float32, accum=accum, w_layout=layout)
     torch.cuda.synchronize()
     y_bits = host_bits16(y_t)[np.ix_(rows, cols)]
     acc_gpu = host(acc_t)[np.ix_(rows, cols)]
@@ -126,31 +127,44 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
 
 
 ACCUMS = ["exact", "mfma_fp8"]
+LAYOUTS = ["row_major", "packed"]
 
 
+def test_pack_weights_is_the_documented_permutation():
+    from test_abi_host import pack_reference
+    rng = np.random.default_rng(1)
+    for n, k in ((37, 384), (16, 128), (1, 256), (300, 1024)):
+        wq = rng.integers(0, 256, (n, k), dtype=np.uint8)
+        got = host(sg.fp8_pack_weights(dev(wq)))
+        assert np.array_equal(got, pack_reference(wq)), (n, k)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("accum", ACCUMS)
-def test_tiny_w8a8(accum):
+def test_tiny_w8a8(accum, layout):
     x, w = tiny_w8a8(0)
-    gemm_case(x, w, accum=accum, what=f"tiny {accum}")
+    gemm_case(x, w, accum=accum, what=f"tiny {accum} {layout}", layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("accum", ACCUMS)
 @pytest.mark.parametrize("m", [1, 8, 32])
-def test_decode_full_size(m, accum):
+def test_decode_full_size(m, accum, layout):
     xb, w, _ = decode_inputs(m)
-    gemm_case(xb, w, accum=accum, what=f"decode M={m} {accum}")
+    gemm_case(xb, w, accum=accum, what=f"decode M={m} {accum} {layout}", layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("accum", ACCUMS)
 @pytest.mark.parametrize("m,n,k", [(300, 1000, 1024), (129, 1001, 256), (17, 515, 128), (33, 4100, 512),
                                    (256, 384, 2048), (1, 7, 128), (5, 1, 384)])
-def test_ragged_tiles(m, n, k, accum):
+def test_ragged_tiles(m, n, k, accum, layout):
     rng = np.random.default_rng(m * 7 + n + k)
     x = rng.standard_normal((m, k)).astype(np.float32)
     x[:, rng.integers(0, k, 2)] *= 40
     from workloads import bf16_bits_from_f32
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
-    gemm_case(bf16_bits_from_f32(x), w, accum=accum, what=f"ragged {m}x{n}x{k} {accum}")
+    gemm_case(bf16_bits_from_f32(x), w, accum=accum, what=f"ragged {m}x{n}x{k} {accum} {layout}", layout=layout)
 
 
 def _sample(M, N, seed, nr=40, nc=384):
@@ -160,12 +174,13 @@ def _sample(M, N, seed, nr=40, nc=384):
     return rows, cols
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("accum", ACCUMS)
 @pytest.mark.parametrize("k", [4096, 14336])
-def test_prefill_full_size_sampled(k, accum):
+def test_prefill_full_size_sampled(k, accum, layout):
     xb, w, _ = prefill_inputs(k)
     rows, cols = _sample(xb.shape[0], w.shape[0], k)
-    gemm_case(xb, w, rows=rows, cols=cols, accum=accum, what=f"prefill K={k} {accum}")
+    gemm_case(xb, w, rows=rows, cols=cols, accum=accum, what=f"prefill K={k} {accum} {layout}", layout=layout)
 
 
 @pytest.mark.parametrize("accum", ACCUMS)
@@ -174,7 +189,9 @@ def test_large_layer_sampled(static, accum):
     xb, w = large_layer_inputs()
     rows, cols = _sample(xb.shape[0], w.shape[0], 4, nr=24, nc=256)
     s = np.float32(STATIC_SCALE_NUM) / np.float32(STATIC_SCALE_DEN) if static else None
-    gemm_case(xb, w, rows=rows, cols=cols, accum=accum, static=s, what=f"large {'static' if static else 'dyn'}")
+    layout = "packed" if static else "row_major"
+    gemm_case(xb, w, rows=rows, cols=cols, accum=accum, static=s, layout=layout,
+              what=f"large {'static' if static else 'dyn'} {layout}")
 
 
 def test_prequantized_input_and_per_tensor_scale():
@@ -197,6 +214,8 @@ def test_deterministic_repeats():
     wq, sw = sg.fp8_quant_weight_per_channel(dev(w))
     xt = dev_bf16(xb)
     outs = [host_bits16(sg.fp8_scaled_gemm(xt, None, wq, sw)) for _ in range(20)]
+    wp = sg.fp8_pack_weights(wq)
+    outs += [host_bits16(sg.fp8_scaled_gemm(xt, None, wp, sw, w_layout="packed")) for _ in range(20)]
     xb2, w2, _ = prefill_inputs(1024, m=512, n=512)
     wq2, sw2 = sg.fp8_quant_weight_per_channel(dev(w2))
     xt2 = dev_bf16(xb2)
