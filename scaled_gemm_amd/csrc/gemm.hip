@@ -16,9 +16,11 @@
 // at byte offset 32 * (lane / 16).  Both operands use this same k assignment,
 // so the products pair up correctly whatever order the hardware sums them in.
 //  * FP8 mode: one v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile and k block.
-//  * Exact mode: the 32 bytes are widened exactly to bf16 (every E4M3 value is a
-//    bf16 value) and fed to four v_mfma_f32_16x16x32_bf16, bytes 8s..8s+7 to
-//    step s.  The bf16 matrix cores form these products exactly and add them at
+//  * Exact mode: the bytes are widened exactly to bf16 (every E4M3 value is a
+//    bf16 value) and fed to the bf16 matrix cores: four v_mfma_f32_16x16x32_bf16
+//    per 16x16 tile (bytes 8s..8s+7 to step s) in the small-M kernels, and
+//    v_mfma_f32_32x32x16_bf16 in the large-tile kernel (lane layout described
+//    there).  The bf16 matrix cores form these products exactly and add them at
 //    fp32 precision, whereas the FP8 matrix cores align each group of 8
 //    products to the group's largest one and drop bits below 2^(e_max - 13).
 #include "fp8_device.h"
@@ -38,18 +40,12 @@ namespace fp8sg {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 struct Frag {  // 32 FP8 bytes
     uint4 lo, hi;
 };
-
-__device__ __forceinline__ Frag zero_frag() {
-    Frag f;
-    f.lo = make_uint4(0, 0, 0, 0);
-    f.hi = f.lo;
-    return f;
-}
 
 __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
     uint32_t u[4] = {e4m3x2_to_bf16x2(w0, false), e4m3x2_to_bf16x2(w0, true), e4m3x2_to_bf16x2(w1, false),
@@ -232,108 +228,351 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Tiled GEMM: 128 (m) x 128 (n) output tile per workgroup, 4 waves in a 2 x 2
-// arrangement of 64 x 64, k in blocks of 128.  Both 128 x 128-byte operand
-// tiles are staged through LDS, double buffered: the global loads of block
-// kb + 1 are in flight while block kb is multiplied.  LDS rows are 128 bytes;
-// the 16-byte chunk c of row r is stored at chunk c ^ (r & 7), so the 16 lanes
-// of a fragment read hit distinct banks.
-constexpr int kTile = 128;
+// Large tiled GEMMs: 256 (m) x 256 (n) output tile per workgroup, 4 waves in a
+// 2 x 2 arrangement of 128 x 128, k in blocks of 128.
+//
+// Operands reach LDS by direct copies from global memory
+// (global_load_lds_dwordx4, no register staging) in matrix-core fragment order:
+// the 16-row x 128-k block of each subtile occupies 2 KB, the 64 lanes' first
+// 16-byte halves and then their second halves, so every fragment read is a
+// lane-contiguous 1 KB ds_read per half, free of bank conflicts.  Two LDS
+// stages: the copy of block kb + 1 is in flight while block kb is multiplied.
+//
+// Workgroups are dealt to the 8 XCDs round-robin; the tile order gives XCD x a
+// contiguous range of tiles, so the workgroups sharing an XCD's L2 share A rows
+// and W columns.  Tiles are ordered in groups of kGroupM m tiles (m fastest
+// within a group): the 32 tiles an XCD holds at once then span 4 m x 8 n tiles,
+// 384 KB of distinct operand bytes per k block instead of 576 KB for 2 x 16.
+constexpr int kBig = 256;
+constexpr int kGroupM = 4;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// s_waitcnt immediate for vmcnt(n), other counters not waited on.
+constexpr int wait_vmcnt(int n) {
+    return 0x0F70 | (n & 15) | ((n >> 4) << 14);
+}
 
-template <bool kFp8, bool kYbf16, bool kWPacked>
-__global__ __launch_bounds__(256, 2) void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
-                                                     int sa_per_token, const uint8_t* __restrict__ W,
-                                                     const float* __restrict__ sw, void* __restrict__ Y, int M,
-                                                     int N, int K) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTile * 128];  // [stage][A=0/W=1]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Per-lane offsets of the 8 one-kilobyte copies wave w issues for one 16-subtile
+// operand tile per stage: copy c = 8 w + i fills half h = c % 2 of subtile
+// j = c / 2.  Row-major operands: subtile row r = lane % 16 of the 16 rows at
+// tile row 16 j, k bytes 32 (lane / 16) + 16 h; rows past the valid count are
+// clamped to the last valid row (their results are never stored).  Packed W:
+// 16-row tile j of the workgroup's tiles (clamped to the last tile), whose k
+// blocks are nkb * 2048 bytes apart.  The offsets are relative to the tile's
+// first row at k = 0 and fit 32 bits for K < 2^24.
+template <bool kPacked>
+__device__ __forceinline__ void tile_copy_offsets(uint32_t (&o)[8], int64_t base_row, int rows, int K, int wave,
+                                                  int lane) {
+    const int r16 = lane & 15, kq = (lane >> 4) * 32;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = wave * 8 + i, j = c >> 1, h = c & 1;
+        if (kPacked) {
+            int64_t t = (base_row >> 4) + j;
+            const int64_t last_tile = ((int64_t)rows + 15) / 16 - 1;
+            t = t < last_tile ? t : last_tile;
+            o[i] = (uint32_t)((t - (base_row >> 4)) * (int64_t)(K >> 7) * kPackBlock + 1024 * h + 16 * lane);
+        } else {
+            int64_t r = base_row + 16 * j + r16;
+            r = r < rows ? r : rows - 1;
+            o[i] = (uint32_t)((r - base_row) * K + kq + 16 * h);
+        }
+    }
+}
+
+// Copy k block kb of one 16-subtile operand tile into LDS (subtile j at
+// lds + 2048 j).  kb_off: kb * 128 for row-major operands, kb * 2048 for packed
+// W.  Each copy is one global_load_lds_dwordx4: lane l's 16 bytes land at
+// M0 + 16 l.
+//
+// The instruction is written out rather than left to the compiler: the compiler
+// cannot tell which LDS bytes a copy writes, so it waits for every copy in
+// flight before any LDS read, which would cap the pipeline at one block.  The
+// kernels order copies and reads themselves: s_waitcnt vmcnt(n) for their own
+// copies, then a workgroup barrier, before reading a stage; a barrier after
+// the last read of a stage before copying into it; vmcnt(0) before exit.  The
+// compiler issues no global loads of its own while copies are in flight.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds_addr), "v"(src)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ void issue_tile_copy(uint8_t* __restrict__ lds, const uint8_t* __restrict__ tile,
+                                                int64_t kb_off, int wave, const uint32_t (&o)[8]) {
+    const uint8_t* base = tile + kb_off;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = wave * 8 + i, j = c >> 1, h = c & 1;
+        copy16_to_lds(base + o[i], lds_base + (uint32_t)(j * kPackBlock + h * 1024));
+    }
+}
+
+// Copy i (0..15) of one stage: A copies 0..7, then W copies 8..15 (subtile
+// layout as in issue_tile_copy).  The kernels spread a stage's 16 copies over
+// the multiplies of a k block: a burst of copies fills the vector-memory queue,
+// and with in-order issue every multiply behind it waits.
+// Copies issued before rows (steps) 1..7: [kCopySplit[i - 1], kCopySplit[i]).
+__device__ constexpr int kCopySplit[8] = {0, 3, 6, 8, 10, 12, 14, 16};
+
+__device__ __forceinline__ void issue_stage_copy(int i, uint8_t* __restrict__ stage, const uint8_t* __restrict__ a_tile,
+                                                 const uint8_t* __restrict__ w_tile, int64_t a_off, int64_t w_off,
+                                                 int wave, const uint32_t (&oa)[8], const uint32_t (&ow)[8]) {
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)stage;
+    const int k = i & 7, c = wave * 8 + k, j = c >> 1, h = c & 1;
+    if (i < 8)
+        copy16_to_lds(a_tile + a_off + oa[k], lds_base + (uint32_t)(j * kPackBlock + h * 1024));
+    else
+        copy16_to_lds(w_tile + w_off + ow[k], lds_base + (uint32_t)((16 + j) * kPackBlock + h * 1024));
+}
+
+__device__ __forceinline__ void tile_coords(int M, int N, int tiles_per_xcd, int& tile, int64_t& m_base,
+                                            int64_t& n_base) {
+    const int tiles_n = (N + kBig - 1) / kBig;
+    const int tiles = ((M + kBig - 1) / kBig) * tiles_n;
+    tile = (int)(blockIdx.x & 7) * tiles_per_xcd + (int)(blockIdx.x >> 3);
+    if (tile >= tiles) {
+        tile = -1;
+        return;
+    }
+    // Groups of kGroupM m tiles: within a group the tiles run m-fastest, so the
+    // 32 workgroups an XCD runs at once cover 4 m tiles x 8 n tiles.
+    const int tiles_m = (M + kBig - 1) / kBig;
+    const int grp = kGroupM * tiles_n;
+    const int first_m = (tile / grp) * kGroupM;
+    const int gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int t = tile % grp;
+    m_base = (int64_t)(first_m + t % gm) * kBig;
+    n_base = (int64_t)(t / gm) * kBig;
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() also orders
+// memory, and for that the compiler waits for every outstanding global load,
+// including the LDS copies meant to stay in flight across the barrier.  The
+// kernels below wait for exactly the copies they need (s_waitcnt) before
+// calling this; the "memory" clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// FP8 mode.  Each wave's 128 x 128 share takes 8 x 8 v_mfma_f32_16x16x128_f8f6f4
+// per k block, with all 256 accumulator registers.  Both operand tiles go
+// through LDS (each W subtile serves the two waves of its column, each A
+// subtile the two waves of its row), so each byte crosses L2 once per
+// workgroup.
+//
+// The copies run two k blocks ahead in two 64 KB stages: once every wave holds
+// block kb's fragments in registers (second barrier), block kb + 2 is copied
+// into the stage they came from while block kb is multiplied.  At the top of
+// step kb the wave waits for its copies of block kb only (vmcnt(16): the 16
+// copies of block kb + 1 stay in flight).  Past the last block the copies
+// repeat block nkb - 1, so the loop body has no branch.
+template <bool kYbf16, bool kWPacked>
+__global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict__ A, const float* __restrict__ sa,
+                                                       int sa_per_token, const uint8_t* __restrict__ W,
+                                                       const float* __restrict__ sw, void* __restrict__ Y, int M,
+                                                       int N, int K, int tiles_per_xcd) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages x (A 32 KB + W 32 KB)
+    constexpr int kStage = 32 * kPackBlock;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave & 1, wn = wave >> 1;
-    const int tiles_n = (N + kTile - 1) / kTile;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-    const int64_t m_base = (int64_t)tm * kTile, n_base = (int64_t)tn * kTile;
+    int tile;
+    int64_t m_base, n_base;
+    tile_coords(M, N, tiles_per_xcd, tile, m_base, n_base);
+    if (tile < 0) return;
     const int nkb = K >> 7;
 
-    // loader: 1024 16-byte chunks per operand tile, 4 per thread.  A (and
-    // row-major W) go to the swizzled row layout; packed W keeps its fragment
-    // order (eight 2048-byte blocks), so its fragment reads are lane-contiguous.
-    const int64_t last_tile = ((int64_t)N + 15) / 16 - 1;
-    uint4 ra[4], rw[4];
-    auto gload = [&](int kb) {
-        const int64_t koff = (int64_t)kb << 7;
+    f32x4 acc[8][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-            const int64_t m = m_base + row;
-            ra[i] = m < M ? *reinterpret_cast<const uint4*>(A + m * K + koff + c * 16) : make_uint4(0, 0, 0, 0);
-            if (kWPacked) {
-                int64_t t = (n_base >> 4) + (id >> 7);
-                t = t < last_tile ? t : last_tile;
-                rw[i] = *reinterpret_cast<const uint4*>(W + (t * nkb + kb) * kPackBlock + (id & 127) * 16);
-            } else {
-                const int64_t n = n_base + row;
-                rw[i] = n < N ? *reinterpret_cast<const uint4*>(W + n * K + koff + c * 16) : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto swrite = [&](int stage) {
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-            *reinterpret_cast<uint4*>(&lds[stage][0][swz(row, c)]) = ra[i];
-            *reinterpret_cast<uint4*>(&lds[stage][1][kWPacked ? id * 16 : swz(row, c)]) = rw[i];
-        }
-    };
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    f32x4 acc[4][4];
+    uint32_t oa[8], ow[8];
+    tile_copy_offsets<false>(oa, m_base, M, K, wave, lane);
+    tile_copy_offsets<kWPacked>(ow, n_base, N, K, wave, lane);
+    const uint8_t* a_tile = A + m_base * K;
+    const uint8_t* w_tile = kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K;
+    const int64_t w_kb = kWPacked ? kPackBlock : 128;
+
+    if (nkb > 0) {
+        const int b1 = nkb > 1 ? 1 : 0;
+        issue_tile_copy(smem, a_tile, 0, wave, oa);
+        issue_tile_copy(smem + 16 * kPackBlock, w_tile, 0, wave, ow);
+        issue_tile_copy(smem + kStage, a_tile, (int64_t)b1 * 128, wave, oa);
+        issue_tile_copy(smem + kStage + 16 * kPackBlock, w_tile, (int64_t)b1 * w_kb, wave, ow);
+    }
+    for (int kb = 0; kb < nkb; ++kb) {
+        uint8_t* cur = smem + (kb & 1) * kStage;
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));  // this wave's copies of block kb have landed
+        barrier_no_fence();                           // ... and every other wave's
+        const uint8_t* la = cur + wm * 8 * kPackBlock;
+        const uint8_t* lw = cur + (16 + wn * 8) * kPackBlock;
+        Frag wf[8], af[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wf[i] = load_frag_packed(lw + i * kPackBlock, lane);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) af[j] = load_frag_packed(la + j * kPackBlock, lane);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[0][j] = mma_fp8(wf[0], af[j], acc[0][j]);
+        __builtin_amdgcn_sched_barrier(0);   // the first row of multiplies overlaps the remaining reads
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all of this wave's fragment reads are done
+        barrier_no_fence();                  // ... and every other wave's: the stage may be refilled
+        const int n = kb + 2 < nkb ? kb + 2 : nkb - 1;
+        const int64_t a_off = (int64_t)n * 128, w_off = (int64_t)n * w_kb;
+        // Rows 1..7 of the multiplies, with the 16 copies of block kb + 2 spread
+        // between them (3, 3, 2, 2, 2, 2, 2 before rows 1..7).
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            const int c0 = kCopySplit[i - 1], c1 = kCopySplit[i];
+#pragma unroll
+            for (int c = c0; c < c1; ++c) issue_stage_copy(c, cur, a_tile, w_tile, a_off, w_off, wave, oa, ow);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = mma_fp8(wf[i], af[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
+
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int64_t m = m_base + wm * 128 + 16 * j + (lane & 15);
+        if (m >= M) continue;
+        const float sam = sa[sa_per_token ? m : 0];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t n0 = n_base + wn * 128 + 16 * i + 4 * (lane >> 4);
+            if (n0 < N) store4<kYbf16>(Y, N, m, n0, acc[i][j], sam, sw, vec_ok);
+        }
+    }
+}
+
+// Exact mode.  The FP8 codes are widened to bf16 (exact) and multiplied by
+// v_mfma_f32_32x32x16_bf16: each wave's 128 x 128 share is 4 x 4 tiles of
+// 32 x 32, 8 steps of 16 k per k block.  Staging and copy schedule as in FP8
+// mode: two stages, copies two blocks ahead, each stage refilled as soon as
+// every wave holds its bytes in registers.
+//
+// Operand lane layout of the 32 x 32 x 16 instruction: lane l supplies row
+// l % 32 and k 8 (l / 32) .. 8 (l / 32) + 7 of the step.  Step s of a k block
+// gives lane l the 8 bytes at offset 8 (s % 4) of the row's 32-byte slice
+// q = 2 (l / 32) + s / 4, i.e. exactly the bytes that lane (l % 16) + 16 q of the
+// row's 16-row subtile holds in the 16 x 16 fragment order of LDS; A and W use
+// the same assignment, so every product pairs matching k.  Output lane layout:
+// acc[r] of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of the tile.
+template <bool kYbf16, bool kWPacked>
+__global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restrict__ A, const float* __restrict__ sa,
+                                                         int sa_per_token, const uint8_t* __restrict__ W,
+                                                         const float* __restrict__ sw, void* __restrict__ Y, int M,
+                                                         int N, int K, int tiles_per_xcd) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages x (A 32 KB + W 32 KB)
+    constexpr int kStage = 32 * kPackBlock;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    int tile;
+    int64_t m_base, n_base;
+    tile_coords(M, N, tiles_per_xcd, tile, m_base, n_base);
+    if (tile < 0) return;
+    const int nkb = K >> 7;
+
+    f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int r16 = lane & 15, c0 = (lane >> 4) * 2;  // this lane's two 16-byte chunks of a row
+    uint32_t oa[8], ow[8];
+    tile_copy_offsets<false>(oa, m_base, M, K, wave, lane);
+    tile_copy_offsets<kWPacked>(ow, n_base, N, K, wave, lane);
+    const uint8_t* a_tile = A + m_base * K;
+    const uint8_t* w_tile = kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K;
+    const int64_t w_kb = kWPacked ? kPackBlock : 128;
+
+    // Byte offset of this lane's first 16-byte half of slice q = 2 (lane / 32)
+    // within a 32-row tile: subtile (lane % 32) / 16, row lane % 16.
+    const int lane_off = ((lane & 31) >> 4) * (int)kPackBlock + (lane & 15) * 16 + (lane >> 5) * 512;
+
     if (nkb > 0) {
-        gload(0);
-        swrite(0);
+        const int b1 = nkb > 1 ? 1 : 0;
+        issue_tile_copy(smem, a_tile, 0, wave, oa);
+        issue_tile_copy(smem + 16 * kPackBlock, w_tile, 0, wave, ow);
+        issue_tile_copy(smem + kStage, a_tile, (int64_t)b1 * 128, wave, oa);
+        issue_tile_copy(smem + kStage + 16 * kPackBlock, w_tile, (int64_t)b1 * w_kb, wave, ow);
     }
-    __syncthreads();
     for (int kb = 0; kb < nkb; ++kb) {
-        const int st = kb & 1;
-        if (kb + 1 < nkb) gload(kb + 1);
-        Frag wf[4], af[4];
+        uint8_t* cur = smem + (kb & 1) * kStage;
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));  // this wave's copies of block kb have landed
+        barrier_no_fence();                           // ... and every other wave's
+        const uint8_t* la = cur + wm * 8 * kPackBlock + lane_off;
+        const uint8_t* lw = cur + (16 + wn * 8) * kPackBlock + lane_off;
+        // raw[g][t][half]: slice q = 2 (lane / 32) + g of tile t (W tiles 0..3, A tiles 4..7)
+        uint4 raw[2][8][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (kWPacked) {
-                wf[i] = load_frag_packed(&lds[st][1][(wn * 4 + i) * kPackBlock], lane);
-            } else {
-                const int rw_ = wn * 64 + 16 * i + r16;
-                wf[i].lo = *reinterpret_cast<const uint4*>(&lds[st][1][swz(rw_, c0)]);
-                wf[i].hi = *reinterpret_cast<const uint4*>(&lds[st][1][swz(rw_, c0 + 1)]);
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint8_t* p = (t < 4 ? lw + 2 * t * kPackBlock : la + 2 * (t - 4) * kPackBlock) + g * 256;
+                raw[g][t][0] = *reinterpret_cast<const uint4*>(p);
+                raw[g][t][1] = *reinterpret_cast<const uint4*>(p + 1024);
             }
-            const int ra_ = wm * 64 + 16 * i + r16;
-            af[i].lo = *reinterpret_cast<const uint4*>(&lds[st][0][swz(ra_, c0)]);
-            af[i].hi = *reinterpret_cast<const uint4*>(&lds[st][0][swz(ra_, c0 + 1)]);
+        auto step = [&](int g, int s4) __attribute__((always_inline)) {
+            bf16x8 v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint4 r = raw[g][t][s4 >> 1];
+                v[t] = (s4 & 1) ? widen8(r.z, r.w) : widen8(r.x, r.y);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[i], v[4 + j], acc[i][j], 0, 0, 0);
+        };
+        step(0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // the first step overlaps the remaining reads
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all of this wave's reads are done
+        barrier_no_fence();                  // ... and every other wave's: the stage may be refilled
+        const int n = kb + 2 < nkb ? kb + 2 : nkb - 1;
+        const int64_t a_off = (int64_t)n * 128, w_off = (int64_t)n * w_kb;
+        // Steps 1..7, with the 16 copies of block kb + 2 spread between them
+        // (3, 3, 2, 2, 2, 2, 2 before steps 1..7).
+#pragma unroll
+        for (int st = 1; st < 8; ++st) {
+            const int c0 = kCopySplit[st - 1], c1 = kCopySplit[st];
+#pragma unroll
+            for (int c = c0; c < c1; ++c) issue_stage_copy(c, cur, a_tile, w_tile, a_off, w_off, wave, oa, ow);
+            __builtin_amdgcn_sched_barrier(0);
+            step(st >> 2, st & 3);
+            __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mma<kFp8>(wf[i], af[j], acc[i][j]);
-        if (kb + 1 < nkb) swrite(st ^ 1);
-        __syncthreads();
     }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
 
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int64_t m = m_base + wm * 64 + 16 * j + r16;
+        const int64_t m = m_base + wm * 128 + 32 * j + (lane & 31);
         if (m >= M) continue;
         const float sam = sa[sa_per_token ? m : 0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t n0 = n_base + wn * 64 + 16 * i + 4 * (lane >> 4);
-            if (n0 < N) store4<kYbf16>(Y, N, m, n0, acc[i][j], sam, sw, vec_ok);
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n0 = n_base + wn * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
+                const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                if (n0 < N) store4<kYbf16>(Y, N, m, n0, v, sam, sw, vec_ok);
+            }
     }
 }
 
@@ -355,9 +594,15 @@ static hipError_t launch_gemm_t(const uint8_t* aq, const float* sa, int sa_pt, c
         launch_skinny<kFp8, kYbf16, kWPacked, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y, M, N, K,
                                                                                      stream);
     } else {
-        const int64_t tiles = (int64_t)((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
-        dim3 grid((unsigned)tiles), block(256);
-        gemm_tiled<kFp8, kYbf16, kWPacked><<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K);
+        const int tiles = ((M + kBig - 1) / kBig) * ((N + kBig - 1) / kBig);
+        const int per = (tiles + 7) / 8;
+        dim3 grid((unsigned)(per * 8)), block(256);
+        if (kFp8)
+            gemm_big_fp8<kYbf16, kWPacked>
+                <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per);
+        else
+            gemm_big_exact<kYbf16, kWPacked>
+                <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per);
     }
     return hipGetLastError();
 }
