@@ -80,18 +80,25 @@ typedef enum fp8sg_accum {
     FP8SG_ACCUM_MFMA_FP8 = 1
 } fp8sg_accum;
 
-/* Memory layout of the E4M3 weight codes given to fp8_scaled_gemm. */
-typedef enum fp8sg_w_layout {
-    /* [N, K] row-major, K contiguous (W_q^T is the column-major "B"). */
+/* Memory layout of the E4M3 operands given to fp8_scaled_gemm: the `layout`
+ * argument is FP8SG_W_ROW_MAJOR (0) or a bitwise OR of the flags below. */
+typedef enum fp8sg_layout {
+    /* Both operands row-major: A_q [M, K] and W_q [N, K], K contiguous (W_q^T is
+     * the column-major "B"). */
     FP8SG_W_ROW_MAJOR = 0,
-    /* Matrix-core fragment order, produced by fp8_pack_weights: rows padded to
-     * a multiple of 16 with zero codes; the 16-row x 128-k block (t, kb) is 2048
-     * contiguous bytes at offset (t * K/128 + kb) * 2048; inside a block, byte
-     * j of lane l's first 16-byte half is at l * 16 + j and of its second half
-     * at 1024 + l * 16 + j, where lane l covers row 16 t + l % 16 and the bytes
-     * [32 (l / 16), 32 (l / 16) + 32) of the block's 128 k. */
-    FP8SG_W_PACKED = 1
-} fp8sg_w_layout;
+    /* W_q in matrix-core fragment order, produced by fp8_pack_weights: rows
+     * padded to a multiple of 16 with zero codes; the 16-row x 128-k block
+     * (t, kb) is 2048 contiguous bytes at offset (t * K/128 + kb) * 2048; inside
+     * a block, byte j of lane l's first 16-byte half is at l * 16 + j and of its
+     * second half at 1024 + l * 16 + j, where lane l covers row 16 t + l % 16
+     * and the bytes [32 (l / 16), 32 (l / 16) + 32) of the block's 128 k. */
+    FP8SG_W_PACKED = 1,
+    /* A_q (a_dtype FP8SG_E4M3 only) in the same fragment order, e.g. from
+     * fp8_pack_weights applied to [M, K] codes: ceil(M / 16) * 16 * K bytes.
+     * Activations that fp8_scaled_gemm quantizes itself always go to its
+     * workspace in this order. */
+    FP8SG_A_PACKED = 2
+} fp8sg_layout;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8sg_status_string(int status);
@@ -143,15 +150,19 @@ fp8sg_status fp8_quant_weight_per_channel(const void* w, int w_dtype, int64_t N,
 size_t fp8_packed_weight_bytes(int64_t N, int64_t K);
 
 /*
- * Reorder row-major E4M3 weight codes [N, K] into FP8SG_W_PACKED (done once,
- * offline, like the quantization itself).  wq and wp are device pointers;
- * wp holds fp8_packed_weight_bytes(N, K) bytes; K % 128 == 0.
+ * Reorder row-major E4M3 codes [N, K] into the fragment order of
+ * FP8SG_W_PACKED (for weights: once, offline, like the quantization itself).
+ * Both GEMM operands share this order, so the same call packs activation
+ * codes [M, K] for FP8SG_A_PACKED.  wq and wp are device pointers; wp holds
+ * fp8_packed_weight_bytes(N, K) bytes; K % 128 == 0.
  */
 fp8sg_status fp8_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, void* stream);
 
 /*
  * Bytes of device workspace fp8_scaled_gemm needs for these arguments (0 when
- * the activation arrives already quantized).  Host-only; no HIP call.
+ * the activation arrives already quantized): the codes it quantizes, in the
+ * fragment order with rows padded to a multiple of 16, then (per-token mode
+ * without a caller buffer) the scales.  Host-only; no HIP call.
  */
 size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, int64_t N, int64_t K);
 
@@ -174,14 +185,16 @@ size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, 
  *   y             [M, N] output, y_dtype FP8SG_BF16 (round to nearest even) or
  *                 FP8SG_F32 (the same epilogue without the bf16 rounding; with
  *                 unit scales this is the raw accumulator)
- *   w_layout      FP8SG_W_ROW_MAJOR or FP8SG_W_PACKED
+ *   layout        FP8SG_W_ROW_MAJOR (0), or an OR of FP8SG_W_PACKED and
+ *                 FP8SG_A_PACKED (the latter only with a_dtype FP8SG_E4M3);
+ *                 other bits: FP8SG_E_DTYPE
  *   accum         FP8SG_ACCUM_EXACT or FP8SG_ACCUM_MFMA_FP8
  *   workspace     device buffer of at least fp8_scaled_gemm_workspace_size(...)
  *                 bytes, 256-byte aligned (may be NULL when that size is 0)
  *   K % 128 == 0; M, N >= 0 arbitrary.
  */
 fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode,
-                             const uint8_t* wq, int w_layout, const float* w_scales, void* y, int y_dtype,
+                             const uint8_t* wq, int layout, const float* w_scales, void* y, int y_dtype,
                              int64_t M, int64_t N, int64_t K, int accum,
                              void* workspace, size_t workspace_bytes, void* stream);
 

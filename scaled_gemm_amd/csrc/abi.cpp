@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -58,7 +58,7 @@ fp8sg_status row_quant(const void* x, int dt, int64_t R, int64_t K, uint8_t* q, 
     fp8sg_status d = device_ok();
     if (d != FP8SG_OK) return d;
     // K == 0 still writes the scales: the maximum of an empty row is 0, so s = 1.0
-    return launched(fp8sg::launch_row_quant(x, dt == FP8SG_BF16, R, K, q, scales, (hipStream_t)stream));
+    return launched(fp8sg::launch_row_quant(x, dt == FP8SG_BF16, R, K, q, scales, false, (hipStream_t)stream));
 }
 
 // Common checks for the [B, S, H, D] KV calls.
@@ -117,10 +117,12 @@ fp8sg_status fp8_quant_per_tensor_static(const void* x, int x_dtype, int64_t num
                                                 fmt == FP8SG_E4M3 ? 0 : 1, q, (hipStream_t)stream));
 }
 
+// Activation codes quantized by fp8_scaled_gemm itself go to the workspace in
+// the fragment order (rows padded to a multiple of 16), then the scales.
 size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, int64_t N, int64_t K) {
     (void)N;
     if (!is_hp(a_dtype) || M <= 0 || K < 0) return 0;
-    size_t bytes = align256((size_t)M * (size_t)K);
+    size_t bytes = align256((size_t)((M + 15) / 16 * 16) * (size_t)K);
     if (a_scale_mode == FP8SG_SCALE_PER_TOKEN) bytes += align256((size_t)M * 4);
     return bytes;
 }
@@ -141,13 +143,14 @@ fp8sg_status fp8_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* 
 }
 
 fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
-                             int w_layout, const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                             int layout, const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                              int accum, void* workspace, size_t workspace_bytes, void* stream) {
     if (!(a_dtype == FP8SG_E4M3 || is_hp(a_dtype))) return FP8SG_E_DTYPE;
     if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
     if (!(a_scale_mode == FP8SG_SCALE_PER_TOKEN || a_scale_mode == FP8SG_SCALE_PER_TENSOR)) return FP8SG_E_DTYPE;
     if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
-    if (!(w_layout == FP8SG_W_ROW_MAJOR || w_layout == FP8SG_W_PACKED)) return FP8SG_E_DTYPE;
+    if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED)) != 0) return FP8SG_E_DTYPE;
+    if ((layout & FP8SG_A_PACKED) && a_dtype != FP8SG_E4M3) return FP8SG_E_DTYPE;  // only codes come packed
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
     if (K % 128 != 0) return FP8SG_E_SHAPE;
     if (M == 0 || N == 0) return FP8SG_OK;
@@ -175,16 +178,18 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
         uint8_t* ws_q = (uint8_t*)workspace;
         hipError_t e;
         if (per_token) {
-            float* sc = a_scales ? a_scales : (float*)((uint8_t*)workspace + align256((size_t)M * (size_t)K));
-            e = fp8sg::launch_row_quant(a, a_dtype == FP8SG_BF16, M, K, ws_q, sc, s);
+            float* sc = a_scales ? a_scales
+                                 : (float*)((uint8_t*)workspace + align256((size_t)((M + 15) / 16 * 16) * (size_t)K));
+            e = fp8sg::launch_row_quant(a, a_dtype == FP8SG_BF16, M, K, ws_q, sc, true, s);
             sa = sc;
         } else {
-            e = fp8sg::launch_grouped_quant(a, a_dtype == FP8SG_BF16, M * K, a_scales, 1, 1, 0, ws_q, s);
+            e = fp8sg::launch_static_quant_packed(a, a_dtype == FP8SG_BF16, M, K, a_scales, ws_q, s);
         }
         if (e != hipSuccess) return FP8SG_E_LAUNCH;
         aq = ws_q;
     }
-    return launched(fp8sg::launch_gemm(aq, sa, per_token, wq, w_layout == FP8SG_W_PACKED, w_scales, y,
+    const bool a_packed = quantize_here || (layout & FP8SG_A_PACKED) != 0;
+    return launched(fp8sg::launch_gemm(aq, a_packed, sa, per_token, wq, (layout & FP8SG_W_PACKED) != 0, w_scales, y,
                                        y_dtype == FP8SG_BF16, M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, s));
 }
 

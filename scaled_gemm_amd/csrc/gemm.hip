@@ -126,7 +126,10 @@ __device__ __forceinline__ void store4(void* y, int64_t N, int64_t m, int64_t n0
 
 // ---------------------------------------------------------------------------
 // Skinny GEMM (M <= 16 * kMT), the decode shape: every byte of W is used once,
-// so W streams from HBM straight into registers.  A workgroup owns kNS 16-row
+// so W streams from HBM straight into registers.  Every workgroup reads all of
+// A (from L2); in the fragment order (kAPacked) each fragment half is one
+// contiguous kilobyte instead of 64-byte pieces of 16 rows, which halves the
+// cache lines touched per load.  A workgroup owns kNS 16-row
 // subtiles of W; its kKS waves split the k blocks round-robin (wave w takes
 // blocks w, w + kKS, ...).  Each wave issues the loads of kDepth of its blocks
 // back to back, then multiplies them, so kDepth * (kNS + kMT) * 32 bytes per lane
@@ -135,7 +138,7 @@ __device__ __forceinline__ void store4(void* y, int64_t N, int64_t m, int64_t n0
 // the compiler wait for each block's loads separately.  The kKS partial sums
 // are added in a fixed order through LDS, so the result does not depend on
 // timing.
-template <bool kFp8, bool kYbf16, int kMT, int kNS, int kKS, int kDepth, bool kWPacked>
+template <bool kFp8, bool kYbf16, int kMT, int kNS, int kKS, int kDepth, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                         int sa_per_token, const uint8_t* __restrict__ W,
                                                         const float* __restrict__ sw, void* __restrict__ Y, int M,
@@ -161,12 +164,17 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
             wrow[s] = W + n * (int64_t)K + kofs;
         }
     }
+    // row-major: this lane's row of each m-tile; packed: the m-tile's first block
     const uint8_t* arow[kMT];
 #pragma unroll
     for (int t = 0; t < kMT; ++t) {
-        int m = 16 * t + r16;
-        m = m < M ? m : M - 1;
-        arow[t] = A + (int64_t)m * K + kofs;
+        if (kAPacked) {
+            arow[t] = A + (int64_t)t * nkb * kPackBlock;
+        } else {
+            int m = 16 * t + r16;
+            m = m < M ? m : M - 1;
+            arow[t] = A + (int64_t)m * K + kofs;
+        }
     }
 
     f32x4 acc[kNS][kMT];
@@ -189,7 +197,8 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
             for (int s = 0; s < kNS; ++s)
                 wf[d][s] = kWPacked ? load_frag_packed(wrow[s] + kb * kPackBlock, lane) : load_frag_global(wrow[s] + off);
 #pragma unroll
-            for (int t = 0; t < kMT; ++t) af[d][t] = load_frag_global(arow[t] + off);
+            for (int t = 0; t < kMT; ++t)
+                af[d][t] = kAPacked ? load_frag_packed(arow[t] + kb * kPackBlock, lane) : load_frag_global(arow[t] + off);
         }
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
@@ -372,7 +381,7 @@ __device__ __forceinline__ void barrier_no_fence() {
 // step kb the wave waits for its copies of block kb only (vmcnt(16): the 16
 // copies of block kb + 1 stay in flight).  Past the last block the copies
 // repeat block nkb - 1, so the loop body has no branch.
-template <bool kYbf16, bool kWPacked>
+template <bool kYbf16, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                        int sa_per_token, const uint8_t* __restrict__ W,
                                                        const float* __restrict__ sw, void* __restrict__ Y, int M,
@@ -395,17 +404,18 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     uint32_t oa[8], ow[8];
-    tile_copy_offsets<false>(oa, m_base, M, K, wave, lane);
+    tile_copy_offsets<kAPacked>(oa, m_base, M, K, wave, lane);
     tile_copy_offsets<kWPacked>(ow, n_base, N, K, wave, lane);
-    const uint8_t* a_tile = A + m_base * K;
+    const uint8_t* a_tile = kAPacked ? A + (m_base >> 4) * (int64_t)nkb * kPackBlock : A + m_base * K;
     const uint8_t* w_tile = kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K;
+    const int64_t a_kb = kAPacked ? kPackBlock : 128;
     const int64_t w_kb = kWPacked ? kPackBlock : 128;
 
     if (nkb > 0) {
         const int b1 = nkb > 1 ? 1 : 0;
         issue_tile_copy(smem, a_tile, 0, wave, oa);
         issue_tile_copy(smem + 16 * kPackBlock, w_tile, 0, wave, ow);
-        issue_tile_copy(smem + kStage, a_tile, (int64_t)b1 * 128, wave, oa);
+        issue_tile_copy(smem + kStage, a_tile, (int64_t)b1 * a_kb, wave, oa);
         issue_tile_copy(smem + kStage + 16 * kPackBlock, w_tile, (int64_t)b1 * w_kb, wave, ow);
     }
     for (int kb = 0; kb < nkb; ++kb) {
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all of this wave's fragment reads are done
         barrier_no_fence();                  // ... and every other wave's: the stage may be refilled
         const int n = kb + 2 < nkb ? kb + 2 : nkb - 1;
-        const int64_t a_off = (int64_t)n * 128, w_off = (int64_t)n * w_kb;
+        const int64_t a_off = (int64_t)n * a_kb, w_off = (int64_t)n * w_kb;
         // Rows 1..7 of the multiplies, with the 16 copies of block kb + 2 spread
         // between them (3, 3, 2, 2, 2, 2, 2 before rows 1..7).
 #pragma unroll
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
 // row's 16-row subtile holds in the 16 x 16 fragment order of LDS; A and W use
 // the same assignment, so every product pairs matching k.  Output lane layout:
 // acc[r] of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of the tile.
-template <bool kYbf16, bool kWPacked>
+template <bool kYbf16, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                          int sa_per_token, const uint8_t* __restrict__ W,
                                                          const float* __restrict__ sw, void* __restrict__ Y, int M,
@@ -493,10 +503,11 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     uint32_t oa[8], ow[8];
-    tile_copy_offsets<false>(oa, m_base, M, K, wave, lane);
+    tile_copy_offsets<kAPacked>(oa, m_base, M, K, wave, lane);
     tile_copy_offsets<kWPacked>(ow, n_base, N, K, wave, lane);
-    const uint8_t* a_tile = A + m_base * K;
+    const uint8_t* a_tile = kAPacked ? A + (m_base >> 4) * (int64_t)nkb * kPackBlock : A + m_base * K;
     const uint8_t* w_tile = kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K;
+    const int64_t a_kb = kAPacked ? kPackBlock : 128;
     const int64_t w_kb = kWPacked ? kPackBlock : 128;
 
     // Byte offset of this lane's first 16-byte half of slice q = 2 (lane / 32)
@@ -507,7 +518,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
         const int b1 = nkb > 1 ? 1 : 0;
         issue_tile_copy(smem, a_tile, 0, wave, oa);
         issue_tile_copy(smem + 16 * kPackBlock, w_tile, 0, wave, ow);
-        issue_tile_copy(smem + kStage, a_tile, (int64_t)b1 * 128, wave, oa);
+        issue_tile_copy(smem + kStage, a_tile, (int64_t)b1 * a_kb, wave, oa);
         issue_tile_copy(smem + kStage + 16 * kPackBlock, w_tile, (int64_t)b1 * w_kb, wave, ow);
     }
     for (int kb = 0; kb < nkb; ++kb) {
@@ -544,7 +555,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all of this wave's reads are done
         barrier_no_fence();                  // ... and every other wave's: the stage may be refilled
         const int n = kb + 2 < nkb ? kb + 2 : nkb - 1;
-        const int64_t a_off = (int64_t)n * 128, w_off = (int64_t)n * w_kb;
+        const int64_t a_off = (int64_t)n * a_kb, w_off = (int64_t)n * w_kb;
         // Steps 1..7, with the 16 copies of block kb + 2 spread between them
         // (3, 3, 2, 2, 2, 2, 2 before steps 1..7).
 #pragma unroll
@@ -576,55 +587,63 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
     }
 }
 
-template <bool kFp8, bool kYbf16, bool kWPacked, int kMT, int kNS, int kKS, int kDepth>
+template <bool kFp8, bool kYbf16, bool kWPacked, bool kAPacked, int kMT, int kNS, int kKS, int kDepth>
 static void launch_skinny(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw, void* y,
                           int M, int N, int K, hipStream_t stream) {
     dim3 grid((unsigned)((N + 16 * kNS - 1) / (16 * kNS))), block(64 * kKS);
-    gemm_skinny<kFp8, kYbf16, kMT, kNS, kKS, kDepth, kWPacked>
+    gemm_skinny<kFp8, kYbf16, kMT, kNS, kKS, kDepth, kWPacked, kAPacked>
         <<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K);
 }
 
-template <bool kFp8, bool kYbf16, bool kWPacked>
+template <bool kFp8, bool kYbf16, bool kWPacked, bool kAPacked>
 static hipError_t launch_gemm_t(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw,
                                 void* y, int M, int N, int K, hipStream_t stream) {
     if (M <= 16) {
-        launch_skinny<kFp8, kYbf16, kWPacked, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y, M, N, K,
-                                                                                     stream);
+        launch_skinny<kFp8, kYbf16, kWPacked, kAPacked, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw,
+                                                                                               y, M, N, K, stream);
     } else if (M <= 32) {
-        launch_skinny<kFp8, kYbf16, kWPacked, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y, M, N, K,
-                                                                                     stream);
+        launch_skinny<kFp8, kYbf16, kWPacked, kAPacked, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw,
+                                                                                               y, M, N, K, stream);
     } else {
         const int tiles = ((M + kBig - 1) / kBig) * ((N + kBig - 1) / kBig);
         const int per = (tiles + 7) / 8;
         dim3 grid((unsigned)(per * 8)), block(256);
         if (kFp8)
-            gemm_big_fp8<kYbf16, kWPacked>
+            gemm_big_fp8<kYbf16, kWPacked, kAPacked>
                 <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per);
         else
-            gemm_big_exact<kYbf16, kWPacked>
+            gemm_big_exact<kYbf16, kWPacked, kAPacked>
                 <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per);
     }
     return hipGetLastError();
 }
 
-template <bool kFp8, bool kWPacked>
+template <bool kFp8, bool kWPacked, bool kAPacked>
 static hipError_t launch_gemm_y(const uint8_t* aq, const float* sa, int pt, const uint8_t* wq, const float* sw, void* y,
                                 bool y_bf16, int M, int N, int K, hipStream_t stream) {
-    return y_bf16 ? launch_gemm_t<kFp8, true, kWPacked>(aq, sa, pt, wq, sw, y, M, N, K, stream)
-                  : launch_gemm_t<kFp8, false, kWPacked>(aq, sa, pt, wq, sw, y, M, N, K, stream);
+    return y_bf16 ? launch_gemm_t<kFp8, true, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, stream)
+                  : launch_gemm_t<kFp8, false, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, stream);
 }
 
-hipError_t launch_gemm(const uint8_t* aq, const float* a_scales, bool a_per_token, const uint8_t* wq, bool w_packed,
-                       const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, bool fp8_mfma,
-                       hipStream_t stream) {
+template <bool kFp8>
+static hipError_t launch_gemm_m(const uint8_t* aq, bool a_packed, const float* sa, int pt, const uint8_t* wq,
+                                bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
+                                hipStream_t stream) {
+    if (a_packed)
+        return w_packed ? launch_gemm_y<kFp8, true, true>(aq, sa, pt, wq, sw, y, y_bf16, M, N, K, stream)
+                        : launch_gemm_y<kFp8, false, true>(aq, sa, pt, wq, sw, y, y_bf16, M, N, K, stream);
+    return w_packed ? launch_gemm_y<kFp8, true, false>(aq, sa, pt, wq, sw, y, y_bf16, M, N, K, stream)
+                    : launch_gemm_y<kFp8, false, false>(aq, sa, pt, wq, sw, y, y_bf16, M, N, K, stream);
+}
+
+hipError_t launch_gemm(const uint8_t* aq, bool a_packed, const float* a_scales, bool a_per_token, const uint8_t* wq,
+                       bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
+                       bool fp8_mfma, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const int pt = a_per_token ? 1 : 0;
     const int m = (int)M, n = (int)N, k = (int)K;
-    if (fp8_mfma)
-        return w_packed ? launch_gemm_y<true, true>(aq, a_scales, pt, wq, w_scales, y, y_bf16, m, n, k, stream)
-                        : launch_gemm_y<true, false>(aq, a_scales, pt, wq, w_scales, y, y_bf16, m, n, k, stream);
-    return w_packed ? launch_gemm_y<false, true>(aq, a_scales, pt, wq, w_scales, y, y_bf16, m, n, k, stream)
-                    : launch_gemm_y<false, false>(aq, a_scales, pt, wq, w_scales, y, y_bf16, m, n, k, stream);
+    if (fp8_mfma) return launch_gemm_m<true>(aq, a_packed, a_scales, pt, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
+    return launch_gemm_m<false>(aq, a_packed, a_scales, pt, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -8,14 +8,19 @@
 
 namespace fp8sg {
 
+// packed: write the codes in the GEMM fragment order (K % 128 == 0) instead of [M, K].
 hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
-                            hipStream_t stream);
+                            bool packed, hipStream_t stream);
+
+// Static per-tensor E4M3 quantization of [M, K] (K % 128 == 0) into the fragment order.
+hipError_t launch_static_quant_packed(const void* x, bool x_is_bf16, int64_t M, int64_t K, const float* scale,
+                                      uint8_t* q, hipStream_t stream);
 
 hipError_t launch_grouped_quant(const void* x, bool x_is_bf16, int64_t numel, const float* scales,
                                 int64_t inner_units, int nscales, int fmt, uint8_t* q, hipStream_t stream);
 
-hipError_t launch_gemm(const uint8_t* aq, const float* a_scales, bool a_per_token, const uint8_t* wq, bool w_packed,
-                       const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
+hipError_t launch_gemm(const uint8_t* aq, bool a_packed, const float* a_scales, bool a_per_token, const uint8_t* wq,
+                       bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
                        bool fp8_mfma, hipStream_t stream);
 
 hipError_t launch_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, hipStream_t stream);

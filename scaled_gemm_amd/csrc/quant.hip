@@ -51,8 +51,19 @@ __device__ __forceinline__ uint2 encode_chunk_dynamic(const float (&v)[8], const
     return o;
 }
 
+// Byte offset of element (m, k) of an [M, K] operand in the matrix-core
+// fragment order shared by both GEMM operands (K % 128 == 0): the 16-row x
+// 128-k block (m / 16, k / 128) is 2048 contiguous bytes; byte j of its 128 k
+// belongs to lane (m % 16) + 16 (j / 32), whose first 16 bytes (j % 32 < 16)
+// sit at lane * 16 and second 16 bytes at 1024 + lane * 16.
+__device__ __forceinline__ int64_t packed_offset(int64_t m, int64_t k, int64_t nkb) {
+    const int j = (int)(k & 127);
+    return (((m >> 4) * nkb + (k >> 7)) << 11) + ((j >> 4) & 1) * 1024 + (((m & 15) + 16 * (j >> 5)) << 4) + (j & 15);
+}
+
 // kChunks chunks per thread held in registers (row length <= kChunks * 8 * blockDim).
-template <typename InT, int kChunks>
+// kPacked: the codes go to the fragment order (packed_offset) instead of [M, K].
+template <typename InT, int kChunks, bool kPacked>
 __global__ __launch_bounds__(256) void row_quant_resident(const InT* __restrict__ x, int64_t K,
                                                           uint8_t* __restrict__ q, float* __restrict__ scales) {
     __shared__ float red[4];
@@ -79,12 +90,15 @@ __global__ __launch_bounds__(256) void row_quant_resident(const InT* __restrict_
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
         const int c = threadIdx.x + i * T;
-        if (c < nchunks) *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) = encode_chunk_dynamic<InT>(v[i], p);
+        if (c < nchunks) {
+            uint8_t* dst = kPacked ? q + packed_offset(row, (int64_t)c * 8, K >> 7) : qr + (int64_t)c * 8;
+            *reinterpret_cast<uint2*>(dst) = encode_chunk_dynamic<InT>(v[i], p);
+        }
     }
 }
 
 // Rows too long for registers: the maximum pass and the encode pass each read the row.
-template <typename InT>
+template <typename InT, bool kPacked>
 __global__ __launch_bounds__(256) void row_quant_stream(const InT* __restrict__ x, int64_t K,
                                                         uint8_t* __restrict__ q, float* __restrict__ scales) {
     __shared__ float red[4];
@@ -106,32 +120,34 @@ __global__ __launch_bounds__(256) void row_quant_stream(const InT* __restrict__ 
     for (int64_t c = threadIdx.x; c < nchunks; c += blockDim.x) {
         float v[8];
         load_chunk<InT>(xr + c * 8, v);
-        *reinterpret_cast<uint2*>(qr + c * 8) = encode_chunk_dynamic<InT>(v, p);
+        uint8_t* dst = kPacked ? q + packed_offset(row, c * 8, K >> 7) : qr + c * 8;
+        *reinterpret_cast<uint2*>(dst) = encode_chunk_dynamic<InT>(v, p);
     }
 }
 
-template <typename InT>
+template <typename InT, bool kPacked>
 static hipError_t launch_row_quant_t(const InT* x, int64_t M, int64_t K, uint8_t* q, float* scales,
                                      hipStream_t stream) {
     const int64_t nchunks = K / 8;
-    int T = (int)((nchunks + 63) / 64 * 64);
-    if (T > 256) T = 256;
-    if (T < 64) T = 64;
+    const int T = 256;
     const int64_t per = (nchunks + T - 1) / T;
     dim3 grid((unsigned)M), block(T);
-    if (per <= 1) row_quant_resident<InT, 1><<<grid, block, 0, stream>>>(x, K, q, scales);
-    else if (per <= 2) row_quant_resident<InT, 2><<<grid, block, 0, stream>>>(x, K, q, scales);
-    else if (per <= 4) row_quant_resident<InT, 4><<<grid, block, 0, stream>>>(x, K, q, scales);
-    else if (per <= 8) row_quant_resident<InT, 8><<<grid, block, 0, stream>>>(x, K, q, scales);
-    else row_quant_stream<InT><<<grid, block, 0, stream>>>(x, K, q, scales);
+    if (per <= 1) row_quant_resident<InT, 1, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
+    else if (per <= 2) row_quant_resident<InT, 2, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
+    else if (per <= 4) row_quant_resident<InT, 4, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
+    else if (per <= 8) row_quant_resident<InT, 8, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
+    else row_quant_stream<InT, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
     return hipGetLastError();
 }
 
 hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
-                            hipStream_t stream) {
+                            bool packed, hipStream_t stream) {
     if (M == 0) return hipSuccess;
-    if (x_is_bf16) return launch_row_quant_t<uint16_t>((const uint16_t*)x, M, K, q, scales, stream);
-    return launch_row_quant_t<float>((const float*)x, M, K, q, scales, stream);
+    if (x_is_bf16)
+        return packed ? launch_row_quant_t<uint16_t, true>((const uint16_t*)x, M, K, q, scales, stream)
+                      : launch_row_quant_t<uint16_t, false>((const uint16_t*)x, M, K, q, scales, stream);
+    return packed ? launch_row_quant_t<float, true>((const float*)x, M, K, q, scales, stream)
+                  : launch_row_quant_t<float, false>((const float*)x, M, K, q, scales, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -221,6 +237,34 @@ hipError_t launch_grouped_quant(const void* x, bool x_is_bf16, int64_t numel, co
         if (fmt == 0) grouped_quant<float, 0><<<grid, block, 0, stream>>>((const float*)x, numel, scales, inner_units, nscales, q);
         else grouped_quant<float, 1><<<grid, block, 0, stream>>>((const float*)x, numel, scales, inner_units, nscales, q);
     }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Static per-tensor quantization of [M, K] activations (K % 128 == 0) straight
+// into the fragment order: one 16-element unit per thread and grid step; the
+// unit's 16 codes are one 16-byte half of one lane (packed_offset).
+template <typename InT>
+__global__ __launch_bounds__(256) void static_quant_packed(const InT* __restrict__ x, int64_t M, int64_t K,
+                                                           const float* __restrict__ scale, uint8_t* __restrict__ q) {
+    const QScale p = make_qscale(scale[0], kE4M3Max);
+    const int64_t upr = K >> 4, nunits = M * upr;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += stride) {
+        const int64_t m = u / upr, k = (u - m * upr) << 4;
+        *reinterpret_cast<uint4*>(q + packed_offset(m, k, K >> 7)) = encode16_given<InT, 0>(x + m * K + k, p);
+    }
+}
+
+hipError_t launch_static_quant_packed(const void* x, bool x_is_bf16, int64_t M, int64_t K, const float* scale,
+                                      uint8_t* q, hipStream_t stream) {
+    if (M == 0 || K == 0) return hipSuccess;
+    const int64_t nunits = M * (K >> 4);
+    int64_t blocks = (nunits + 255) / 256;
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    dim3 grid((unsigned)blocks), block(256);
+    if (x_is_bf16) static_quant_packed<uint16_t><<<grid, block, 0, stream>>>((const uint16_t*)x, M, K, scale, q);
+    else static_quant_packed<float><<<grid, block, 0, stream>>>((const float*)x, M, K, scale, q);
     return hipGetLastError();
 }
 

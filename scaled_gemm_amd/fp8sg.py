@@ -26,7 +26,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8sg.h")
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_DEVICE, E_LAUNCH, E_WORKSPACE = range(8)
 F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
 SCALE_PER_TOKEN, SCALE_PER_TENSOR = 0, 1
-W_ROW_MAJOR, W_PACKED = 0, 1
+W_ROW_MAJOR, W_PACKED, A_PACKED = 0, 1, 2
 ACCUM_EXACT, ACCUM_MFMA_FP8 = 0, 1
 
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
@@ -187,23 +187,33 @@ def fp8_scaled_gemm_workspace_size(a_dtype, a_scale_mode, M: int, N: int, K: int
 
 def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor, w_scales: torch.Tensor, *,
                     a_scale_mode="per_token", out_dtype=torch.bfloat16, accum="exact", w_layout="row_major",
-                    y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
+                    a_layout="row_major", a_shape: Optional[tuple] = None, y: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Y [M, N] = diag(s_a) (A_q W_q^T) diag(s_w).
 
     a: uint8 E4M3 codes [M, K] (a_scales is then an input), or bf16/fp32
     activations that the call quantizes first (per token: a_scales, if given,
     receives the computed scales; per tensor: a_scales [1] is the given scale).
+    a_layout="packed": a is the 1-D fragment-order buffer of fp8_pack_weights
+    applied to the [M, K] codes, and a_shape=(M, K) gives the shape.
     wq: [N, K] row-major codes, or (w_layout="packed") the 1-D buffer of
     fp8_pack_weights; N is taken from w_scales.
     """
     _need(a, "a", (torch.uint8, torch.bfloat16, torch.float32))
     _need(wq, "wq", (torch.uint8,))
     _need(w_scales, "w_scales", (torch.float32,))
-    M, K = a.shape
+    a_packed = _LAYOUT[a_layout] == W_PACKED
+    if a_packed:
+        if a.dtype != torch.uint8 or a_shape is None:
+            raise ValueError("a_layout='packed' takes E4M3 codes and a_shape=(M, K)")
+        M, K = (int(v) for v in a_shape)
+        if a.numel() != fp8_packed_weight_bytes(M, K):
+            raise ValueError(f"packed a has {a.numel()} bytes, expected {fp8_packed_weight_bytes(M, K)}")
+    else:
+        M, K = a.shape
     N = w_scales.shape[0]
-    layout = _LAYOUT[w_layout]
-    if layout == W_ROW_MAJOR:
+    layout = _LAYOUT[w_layout] | (A_PACKED if a_packed else 0)
+    if _LAYOUT[w_layout] == W_ROW_MAJOR:
         if tuple(wq.shape) != (N, K):
             raise ValueError(f"wq has shape {tuple(wq.shape)}, expected {(N, K)}")
     elif wq.numel() != fp8_packed_weight_bytes(N, K):

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert sg.lib().fp8sg_version() == 2
+    assert sg.lib().fp8sg_version() == 3
     for st in range(8):
         assert sg.status_string(st)
     assert sg.status_string(99) == "unknown status"
@@ -76,7 +76,10 @@ def test_gemm_validation(lib):
         return g(d["a"], d["a_dt"], d["sa"], d["mode"], d["wq"], d["lay"], d["sw"], d["y"], d["y_dt"], d["M"], d["N"],
                  d["K"], d["accum"], d["ws"], d["wsb"], None)
 
-    assert call(lay=2) == b.E_DTYPE
+    assert call(lay=4) == b.E_DTYPE
+    assert call(lay=b.W_PACKED | 4) == b.E_DTYPE
+    # packed activation codes only: high-precision activations are row-major
+    assert call(lay=b.A_PACKED, a_dt=b.BF16) == b.E_DTYPE
     assert call(K=100) == b.E_SHAPE
     assert call(a_dt=b.E5M2) == b.E_DTYPE
     assert call(y_dt=b.E4M3) == b.E_DTYPE
@@ -86,11 +89,13 @@ def test_gemm_validation(lib):
     assert call(wq=None) == b.E_NULL
     assert call(y=A + 4) == b.E_ALIGN
     assert call(M=0) == b.OK
-    # a bf16 activation needs the workspace the size query reports
+    # a bf16 activation needs the workspace the size query reports: the codes in
+    # the fragment order (rows padded to 16), then the per-token scales
     need = lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4, 8, 128)
-    assert need == 512 + 256
+    assert need == 16 * 128 + 256
     assert lib.fp8_scaled_gemm_workspace_size(b.E4M3, b.SCALE_PER_TOKEN, 4, 8, 128) == 0
-    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TENSOR, 4, 8, 128) == 512
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TENSOR, 4, 8, 128) == 16 * 128
+    assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TENSOR, 33, 8, 256) == 48 * 256
     assert call(a_dt=b.BF16, sa=None) == b.E_WORKSPACE
     assert call(a_dt=b.BF16, sa=None, ws=A, wsb=need - 1) == b.E_WORKSPACE
     assert call(a_dt=b.BF16, sa=None, ws=A + 16, wsb=need) == b.E_ALIGN

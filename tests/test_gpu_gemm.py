@@ -120,9 +120,17 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
     ones_m = torch.ones(M, dtype=torch.float32, device="cuda")
     ones_n = torch.ones(N, dtype=torch.float32, device="cuda")
     acc_t = sg.fp8_scaled_gemm(aq_t, ones_m, wg, ones_n, out_dtype=torch.float32, accum=accum, w_layout=layout)
+    # the same codes in the fragment order (FP8SG_A_PACKED): the kernels give each
+    # lane the same k, so the accumulators must agree bit for bit
+    ap_t = sg.fp8_pack_weights(aq_t)
+    acc_p = sg.fp8_scaled_gemm(ap_t, ones_m, wg, ones_n, out_dtype=torch.float32, accum=accum, w_layout=layout,
+                               a_layout="packed", a_shape=(M, K))
     torch.cuda.synchronize()
     y_bits = host_bits16(y_t)[np.ix_(rows, cols)]
     acc_gpu = host(acc_t)[np.ix_(rows, cols)]
+    acc_pk = host(acc_p)[np.ix_(rows, cols)]
+    assert np.array_equal(acc_pk.view(np.uint32), acc_gpu.view(np.uint32)), f"{what}: packed-A accumulator differs"
+    del ap_t, acc_p
     check_outputs(y_bits, acc_gpu, aq_ref, sa_ref, wq_ref, sw_ref, accum, what)
 
 
