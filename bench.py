@@ -12,8 +12,9 @@ The weights rotate through enough copies (8 x 58.7 MB) that the 256 MB
 last-level cache cannot serve them.
 
 `roofline` is for the step's dominant kernel, the skinny GEMM of the M = 32
-call, timed per launch with HIP events on the library's stream (pre-quantized
-activations, so the GEMM kernel is the only kernel between the events).
+call, timed per launch with HIP events on the library's stream (activations
+pre-quantized and packed into the fragment order the fused call's workspace
+uses, so the GEMM kernel is the only kernel between the events).
 `cpu_baseline` times the CPU oracle on the same decode workload.
 `details` carries every other measured workload (prefill and large-layer GEMMs
 in both accumulation modes, the quantizers, the KV-cache passes).
@@ -39,6 +40,19 @@ METRIC = "fp8_scaled_gemm TFLOPS + quant GB/s at 1 MI355X, as % of MFMA/HBM peak
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # dense FP8 matrix cores
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
+# HBM traffic of the roofline kernel from two rocprofv3 counter passes over
+# `bench.py --quick --no-cpu --pmc-calibrate` (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch, median over the dispatches), each scaled by what the counter
+# reads for the 1 GiB calibration copy (FETCH_SIZE reads half the copy's bytes
+# on this part, WRITE_SIZE all of them).  Valid only for the kernel source it
+# was measured on: when the hash of these files differs, traffic is reported
+# as null until the counters are taken again.
+TRAFFIC = {"kernel": "gemm_skinny<false, true, 2, 2, 4, 2, true, true>",
+           "sources": ("scaled_gemm_amd/csrc/gemm.hip", "scaled_gemm_amd/csrc/fp8_device.h"),
+           "sha256": ("aa6dec82f3f48996a8d61aabbe44e420ae8427dce04d4826bdef70dedbbc4bee",
+                      "64ef8929298736914d816d7e5a5c2adfb7fed06096440615cefb291c61b53d78"),
+           "fetch_kib": 29255.0, "write_kib": 896.2,
+           "fetch_factor": 1048576.0 / 524315.4, "write_factor": 1048576.0 / 1048576.0}
 DEC_N, DEC_K = 14336, 4096
 DEC_MS = (1, 8, 32)
 W_COPIES = 8
@@ -152,15 +166,22 @@ def main():
     kern = {}
     for m in DEC_MS:
         aq, sa = sg.fp8_quant_per_token(xs[m])
-        for layout, bufs in (("packed", wqs), ("row_major", wrm)):
+        # the fused call quantizes into its workspace in the fragment order; the
+        # same codes packed here let the GEMM kernel be timed on its own
+        ap = sg.fp8_pack_weights(aq)
+        for layout, bufs, a_layout in (("packed", wqs, "packed"), ("packed", wqs, "row_major"),
+                                       ("row_major", wrm, "row_major")):
+            a_in = ap if a_layout == "packed" else aq
             for accum in ("exact", "mfma_fp8"):
-                d = timed_events(lambda i: sg.fp8_scaled_gemm(aq, sa, bufs[i % W_COPIES], sw, y=ys[m], accum=accum,
-                                                              w_layout=layout), 100, 20)
+                d = timed_events(lambda i: sg.fp8_scaled_gemm(a_in, sa, bufs[i % W_COPIES], sw, y=ys[m], accum=accum,
+                                                              w_layout=layout, a_layout=a_layout,
+                                                              a_shape=(m, DEC_K)), 100, 20)
                 # algorithmic bytes of the GEMM kernel alone: W + s_w + A_q + s_a + Y
                 kb = DEC_N * DEC_K + 4 * DEC_N + m * DEC_K + 4 * m + 2 * m * DEC_N
-                kern[(m, accum, layout)] = (kb, float(d.mean()))
+                kern[(m, accum, layout, a_layout)] = (kb, float(d.mean()))
                 details.append({"workload": f"decode GEMM kernel M={m} N={DEC_N} K={DEC_K} (pre-quantized A)",
-                                "accum": accum, "w_layout": layout, "avg_us": round(float(d.mean()) * 1e3, 2),
+                                "accum": accum, "w_layout": layout, "a_layout": a_layout,
+                                "avg_us": round(float(d.mean()) * 1e3, 2),
                                 "min_us": round(float(np.min(d)) * 1e3, 2),
                                 "GB_s": round(kb / (d.mean() * 1e-3) / 1e9, 1),
                                 "frac_hbm": round(kb / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
@@ -169,11 +190,11 @@ def main():
         details.append({"workload": f"decode call M={m} (fused per-token quant + GEMM)", "accum": "exact",
                         "w_layout": "packed", "avg_us": round(float(d.mean()) * 1e3, 2),
                         "GB_s": round(bytes_per_call[m] / (d.mean() * 1e-3) / 1e9, 1)})
-    kb32, dur32 = kern[(32, "exact", "packed")]
+    kb32, dur32 = kern[(32, "exact", "packed", "packed")]
     achieved = kb32 / (dur32 * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemm_skinny<exact, bf16 out, 2 m-tiles, packed W> (decode M=32)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "kernel": "gemm_skinny<exact, bf16 out, 2 m-tiles, packed W, packed A> (decode M=32)",
                 "avg_launch_us": round(dur32 * 1e3, 2), "bytes_per_launch": kb32,
                 "timing": "HIP events around 100 back-to-back launches on the library's stream, mean of 5"}
 
@@ -214,6 +235,18 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel from the recorded counters,
+    or None when its source has changed since they were taken."""
+    import hashlib
+    for rel, want in zip(TRAFFIC["sources"], TRAFFIC["sha256"]):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != want:
+                return None
+    return int(round(1024 * (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_factor"] +
+                             TRAFFIC["write_kib"] * TRAFFIC["write_factor"])))
+
+
 def _gbs(nbytes, ms):
     return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
@@ -241,17 +274,22 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
             sa = torch.tensor([static_scale], dtype=torch.float32, device=dev)
             aq = sg.fp8_quant_per_tensor_static(x_list[0], sa)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        for accum, layout, wbuf in (("exact", "packed", wq), ("mfma_fp8", "packed", wq), ("exact", "row_major", wq_rm)):
-            d = timed_events(lambda i: sg.fp8_scaled_gemm(aq, sa, wbuf, sw, y=y, accum=accum, w_layout=layout,
+        ap = sg.fp8_pack_weights(aq)  # the fragment order the fused call's workspace uses
+        for accum, layout, wbuf, a_layout in (("exact", "packed", wq, "packed"), ("mfma_fp8", "packed", wq, "packed"),
+                                              ("exact", "row_major", wq_rm, "row_major")):
+            a_in = ap if a_layout == "packed" else aq
+            d = timed_events(lambda i: sg.fp8_scaled_gemm(a_in, sa, wbuf, sw, y=y, accum=accum, w_layout=layout,
+                                                          a_layout=a_layout, a_shape=(M, K),
                                                           a_scale_mode="per_token" if static_scale is None
                                                           else "per_tensor"), 10, 3, reps=3)
             tf = _tflops(flops, d.mean())
             row = {"workload": f"{tag} GEMM {M}x{N}x{K} (pre-quantized A)", "accum": accum, "w_layout": layout,
-                   "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
+                   "a_layout": a_layout, "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
                    "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
             if accum == "exact":
                 row["frac_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
             out.append(row)
+        del ap
         ws = torch.empty(sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", M, N, K), dtype=torch.uint8,
                          device=dev)
         mode = "per_token" if static_scale is None else "per_tensor"

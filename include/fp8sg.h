@@ -95,8 +95,8 @@ typedef enum fp8sg_layout {
     FP8SG_W_PACKED = 1,
     /* A_q (a_dtype FP8SG_E4M3 only) in the same fragment order, e.g. from
      * fp8_pack_weights applied to [M, K] codes: ceil(M / 16) * 16 * K bytes.
-     * Activations that fp8_scaled_gemm quantizes itself always go to its
-     * workspace in this order. */
+     * Activations that fp8_scaled_gemm quantizes itself go to its workspace
+     * in this order when M <= 32. */
     FP8SG_A_PACKED = 2
 } fp8sg_layout;
 
@@ -161,8 +161,9 @@ fp8sg_status fp8_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* 
 /*
  * Bytes of device workspace fp8_scaled_gemm needs for these arguments (0 when
  * the activation arrives already quantized): the codes it quantizes, in the
- * fragment order with rows padded to a multiple of 16, then (per-token mode
- * without a caller buffer) the scales.  Host-only; no HIP call.
+ * fragment order with rows padded to a multiple of 16 when M <= 32, row-major
+ * otherwise, then (per-token mode without a caller buffer) the scales.
+ * Host-only; no HIP call.
  */
 size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, int64_t N, int64_t K);
 

@@ -117,12 +117,22 @@ fp8sg_status fp8_quant_per_tensor_static(const void* x, int x_dtype, int64_t num
                                                 fmt == FP8SG_E4M3 ? 0 : 1, q, (hipStream_t)stream));
 }
 
-// Activation codes quantized by fp8_scaled_gemm itself go to the workspace in
-// the fragment order (rows padded to a multiple of 16), then the scales.
+// Activation codes quantized by fp8_scaled_gemm itself go to the workspace,
+// then the scales.  Decode-sized activations (M <= 32, the skinny kernel, which
+// reads all of A in every workgroup) are written in the fragment order, rows
+// padded to 16; larger ones row-major: there one workgroup quantizes one row,
+// and in the fragment order its stores would scatter over 8x more cache lines.
+constexpr int64_t kPackedAMaxM = 32;
+
+size_t quantized_a_bytes(int64_t M, int64_t K) {
+    const int64_t rows = M <= kPackedAMaxM ? (M + 15) / 16 * 16 : M;
+    return align256((size_t)rows * (size_t)K);
+}
+
 size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, int64_t N, int64_t K) {
     (void)N;
     if (!is_hp(a_dtype) || M <= 0 || K < 0) return 0;
-    size_t bytes = align256((size_t)((M + 15) / 16 * 16) * (size_t)K);
+    size_t bytes = quantized_a_bytes(M, K);
     if (a_scale_mode == FP8SG_SCALE_PER_TOKEN) bytes += align256((size_t)M * 4);
     return bytes;
 }
@@ -158,6 +168,7 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
     if (K > 0 && (!a || !wq)) return FP8SG_E_NULL;
     const bool per_token = a_scale_mode == FP8SG_SCALE_PER_TOKEN;
     const bool quantize_here = is_hp(a_dtype);
+    const bool pack_here = quantize_here && M <= kPackedAMaxM;
     if (!quantize_here || !per_token) {
         if (!a_scales) return FP8SG_E_NULL;  // an input in these modes
     }
@@ -178,17 +189,18 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
         uint8_t* ws_q = (uint8_t*)workspace;
         hipError_t e;
         if (per_token) {
-            float* sc = a_scales ? a_scales
-                                 : (float*)((uint8_t*)workspace + align256((size_t)((M + 15) / 16 * 16) * (size_t)K));
-            e = fp8sg::launch_row_quant(a, a_dtype == FP8SG_BF16, M, K, ws_q, sc, true, s);
+            float* sc = a_scales ? a_scales : (float*)((uint8_t*)workspace + quantized_a_bytes(M, K));
+            e = fp8sg::launch_row_quant(a, a_dtype == FP8SG_BF16, M, K, ws_q, sc, pack_here, s);
             sa = sc;
-        } else {
+        } else if (pack_here) {
             e = fp8sg::launch_static_quant_packed(a, a_dtype == FP8SG_BF16, M, K, a_scales, ws_q, s);
+        } else {
+            e = fp8sg::launch_grouped_quant(a, a_dtype == FP8SG_BF16, M * K, a_scales, 1, 1, 0, ws_q, s);
         }
         if (e != hipSuccess) return FP8SG_E_LAUNCH;
         aq = ws_q;
     }
-    const bool a_packed = quantize_here || (layout & FP8SG_A_PACKED) != 0;
+    const bool a_packed = quantize_here ? pack_here : (layout & FP8SG_A_PACKED) != 0;
     return launched(fp8sg::launch_gemm(aq, a_packed, sa, per_token, wq, (layout & FP8SG_W_PACKED) != 0, w_scales, y,
                                        y_dtype == FP8SG_BF16, M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, s));
 }
