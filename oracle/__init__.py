@@ -12,8 +12,10 @@ Modules:
   w8a8   -- per-token, per-tensor and per-channel quantizers; exact GEMM
             accumulator and scaled bf16 output
   kv     -- KV-cache calibrate / quantize / dequantize / append
+  blockwise -- 1 x 128 activation groups, 128 x 128 weight blocks, and the
+            GEMM that scales each 128-deep partial sum by its own scales
   native -- the same encoder in plain C (oracle/c/fp8_oracle.c) for sweeps
             over every float32 bit pattern; loaded from its built library
 """
 
-from . import fp8, kv, w8a8  # noqa: F401
+from . import blockwise, fp8, kv, w8a8  # noqa: F401
