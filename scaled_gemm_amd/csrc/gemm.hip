@@ -33,7 +33,7 @@
 #define SKINNY_KS 4
 #endif
 #ifndef SKINNY_DEPTH
-#define SKINNY_DEPTH 2
+#define SKINNY_DEPTH 1
 #endif
 
 namespace fp8sg {
@@ -94,12 +94,30 @@ __device__ __forceinline__ Frag load_frag_packed(const uint8_t* block, int lane)
 }
 
 // Epilogue for one 16x16 fragment: lane holds acc[r] = C[n0 + r][m], r = 0..3.
+// store4 applies the per-token / per-channel scales; store4_raw stores the
+// values as they are (block-wise scales were applied inside the k loop).
+template <bool kYbf16>
+__device__ __forceinline__ void store4_vals(void* y, int64_t N, int64_t m, int64_t n0, const float (&v)[4],
+                                           bool vec_ok);
+
+template <bool kYbf16>
+__device__ __forceinline__ void store4_raw(void* y, int64_t N, int64_t m, int64_t n0, f32x4 acc, bool vec_ok) {
+    const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+    store4_vals<kYbf16>(y, N, m, n0, v, vec_ok);
+}
+
 template <bool kYbf16>
 __device__ __forceinline__ void store4(void* y, int64_t N, int64_t m, int64_t n0, f32x4 acc, float sa,
                                        const float* __restrict__ sw, bool vec_ok) {
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = (n0 + r < N) ? (acc[r] * sa) * sw[n0 + r] : 0.0f;
+    store4_vals<kYbf16>(y, N, m, n0, v, vec_ok);
+}
+
+template <bool kYbf16>
+__device__ __forceinline__ void store4_vals(void* y, int64_t N, int64_t m, int64_t n0, const float (&v)[4],
+                                           bool vec_ok) {
     if (kYbf16) {
         uint16_t* yr = (uint16_t*)y + m * N;
         if (vec_ok && n0 + 3 < N) {
@@ -138,7 +156,13 @@ __device__ __forceinline__ void store4(void* y, int64_t N, int64_t m, int64_t n0
 // the compiler wait for each block's loads separately.  The kKS partial sums
 // are added in a fixed order through LDS, so the result does not depend on
 // timing.
-template <bool kFp8, bool kYbf16, int kMT, int kNS, int kKS, int kDepth, bool kWPacked, bool kAPacked>
+//
+// kBlock: block-wise scales, sa [M, K / 128] and sw [ceil(N / 128), K / 128].
+// Each k block's 16 x 16 partial products start from zero, are multiplied by
+// s_a[m, kb] * s_w[n / 128, kb] and added to the fp32 accumulator, so the
+// epilogue only rounds.  A 16-row subtile never straddles a 128-row block.
+template <bool kFp8, bool kYbf16, int kMT, int kNS, int kKS, int kDepth, bool kWPacked, bool kAPacked,
+          bool kBlock = false>
 __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                         int sa_per_token, const uint8_t* __restrict__ W,
                                                         const float* __restrict__ sw, void* __restrict__ Y, int M,
@@ -183,10 +207,27 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
 #pragma unroll
         for (int t = 0; t < kMT; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // block-wise scales: this lane's rows of s_a and the subtiles' rows of s_w
+    const float* sa_row[kMT];
+    const float* sw_row[kNS];
+    if (kBlock) {
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) {
+            const int m = 16 * t + r16 < M ? 16 * t + r16 : M - 1;
+            sa_row[t] = sa + (int64_t)m * nkb;
+        }
+#pragma unroll
+        for (int s = 0; s < kNS; ++s) {
+            const int64_t n = n_base + 16 * s < N ? n_base + 16 * s : N - 1;
+            sw_row[s] = sw + (n >> 7) * nkb;
+        }
+    }
+
     // this wave's blocks: wave + j * kKS, j < nper
     const int nper = nkb > wave ? (nkb - wave + kKS - 1) / kKS : 0;
     for (int j0 = 0; j0 < nper; j0 += kDepth) {
         Frag wf[kDepth][kNS], af[kDepth][kMT];
+        float fa[kDepth][kMT], fw[kDepth][kNS];
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             int j = j0 + d;
@@ -199,6 +240,12 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
 #pragma unroll
             for (int t = 0; t < kMT; ++t)
                 af[d][t] = kAPacked ? load_frag_packed(arow[t] + kb * kPackBlock, lane) : load_frag_global(arow[t] + off);
+            if (kBlock) {
+#pragma unroll
+                for (int t = 0; t < kMT; ++t) fa[d][t] = sa_row[t][kb];
+#pragma unroll
+                for (int s = 0; s < kNS; ++s) fw[d][s] = sw_row[s][kb];
+            }
         }
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
@@ -206,7 +253,16 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
 #pragma unroll
                 for (int s = 0; s < kNS; ++s)
 #pragma unroll
-                    for (int t = 0; t < kMT; ++t) acc[s][t] = mma<kFp8>(wf[d][s], af[d][t], acc[s][t]);
+                    for (int t = 0; t < kMT; ++t) {
+                        if (kBlock) {
+                            const f32x4 p = mma<kFp8>(wf[d][s], af[d][t], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                            const float f = fa[d][t] * fw[d][s];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[s][t][r] = __builtin_fmaf(p[r], f, acc[s][t][r]);
+                        } else {
+                            acc[s][t] = mma<kFp8>(wf[d][s], af[d][t], acc[s][t]);
+                        }
+                    }
             }
         }
     }
@@ -231,7 +287,10 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
                 for (int w = 0; w < kKS - 1; ++w) v += red[w][s * kMT + t][lane];
                 const int m = 16 * t + r16;
                 const int64_t n0 = n_base + 16 * s + 4 * (lane >> 4);
-                if (m < M && n0 < N) store4<kYbf16>(Y, N, m, n0, v, sa[sa_per_token ? m : 0], sw, vec_ok);
+                if (m < M && n0 < N) {
+                    if (kBlock) store4_raw<kYbf16>(Y, N, m, n0, v, vec_ok);
+                    else store4<kYbf16>(Y, N, m, n0, v, sa[sa_per_token ? m : 0], sw, vec_ok);
+                }
             }
     }
 }
@@ -369,6 +428,62 @@ __device__ __forceinline__ void barrier_no_fence() {
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Epilogue of the large-tile kernels for bf16 output.  A matrix-core result
+// fragment gives each lane four consecutive n of one row m, so storing
+// fragments directly writes 32-byte pieces of 16 different rows per
+// instruction, and the write path, not the multiplies, then dominates short-K
+// tiles.  Instead each wave scales and rounds its 128 x 128 share, stages it in
+// LDS row-major (256 bytes per row), and stores whole 256-byte row segments:
+// one instruction covers four rows.  The 16-byte column slots of a row are
+// permuted by XOR with the row's low four bits, so the 16 rows one fragment
+// writes fall on different banks, and a row read back is still 16 slots.
+constexpr int kEpiRowBytes = 256;
+constexpr int kEpiWaveBytes = 128 * kEpiRowBytes;  // 32 KB per wave, 128 KB per workgroup
+static_assert(4 * kEpiWaveBytes <= 2 * 32 * kPackBlock, "the staged output reuses the two operand stages");
+
+__device__ __forceinline__ uint32_t epi_offset(int row, int col_bytes) {
+    return (uint32_t)(row * kEpiRowBytes + (col_bytes ^ ((row & 15) << 4)));
+}
+
+// Row `row`, columns col .. col + 3 (col % 4 == 0) of the wave's staged tile.
+__device__ __forceinline__ void epi_put4(uint8_t* wl, int row, int col, float v0, float v1, float v2, float v3) {
+    uint2 o;
+    o.x = pack_bf16x2(v0, v1);
+    o.y = pack_bf16x2(v2, v3);
+    *reinterpret_cast<uint2*>(wl + epi_offset(row, col * 2)) = o;
+}
+
+// Store the wave's staged kRows x 128 tile to Y rows m0.., columns n0.. .
+template <int kRows = 128>
+__device__ __forceinline__ void epi_store(const uint8_t* wl, uint16_t* __restrict__ Y, int64_t M, int64_t N,
+                                          int64_t m0, int64_t n0, int lane) {
+    const int c = lane & 15;
+    const int64_t n = n0 + 8 * c;
+    const bool vec = (N & 7) == 0 && n + 8 <= N;
+#pragma unroll 4
+    for (int it = 0; it < kRows / 4; ++it) {
+        const int row = 4 * it + (lane >> 4);
+        const int64_t m = m0 + row;
+        if (m >= M) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(wl + epi_offset(row, 16 * c));
+        uint16_t* yr = Y + m * N;
+        if (vec) {
+            *reinterpret_cast<uint4*>(yr + n) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) yr[n + e] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
+    }
+}
+
+// The four per-channel scales of columns n0 .. n0 + 3 (0 past N).
+__device__ __forceinline__ void load_sw4(const float* __restrict__ sw, int64_t N, int64_t n0, float (&v)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = n0 + r < N ? sw[n0 + r] : 0.0f;
+}
+
 // FP8 mode.  Each wave's 128 x 128 share takes 8 x 8 v_mfma_f32_16x16x128_f8f6f4
 // per k block, with all 256 accumulator registers.  Both operand tiles go
 // through LDS (each W subtile serves the two waves of its column, each A
@@ -451,6 +566,31 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
 
+    if (kYbf16) {
+        __syncthreads();  // every wave is done with the stages: the LDS now holds the output tiles
+        uint8_t* wl = smem + wave * kEpiWaveBytes;
+        float sam[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int64_t m = m_base + wm * 128 + 16 * j + (lane & 15);
+            m = m < M ? m : M - 1;
+            sam[j] = sa[sa_per_token ? m : 0];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float s4[4];
+            load_sw4(sw, N, n_base + wn * 128 + 16 * i + 4 * (lane >> 4), s4);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const f32x4 a = acc[i][j];
+                epi_put4(wl, 16 * j + (lane & 15), 16 * i + 4 * (lane >> 4), (a[0] * sam[j]) * s4[0],
+                         (a[1] * sam[j]) * s4[1], (a[2] * sam[j]) * s4[2], (a[3] * sam[j]) * s4[3]);
+            }
+        }
+        __syncthreads();
+        epi_store(wl, (uint16_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
+        return;
+    }
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -570,6 +710,35 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
 
+    if (kYbf16) {
+        __syncthreads();  // every wave is done with the stages: the LDS now holds the output tiles
+        uint8_t* wl = smem + wave * kEpiWaveBytes;
+        float sam[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int64_t m = m_base + wm * 128 + 32 * j + (lane & 31);
+            m = m < M ? m : M - 1;
+            sam[j] = sa[sa_per_token ? m : 0];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = 32 * i + 8 * g + 4 * (lane >> 5);
+                float s4[4];
+                load_sw4(sw, N, n_base + wn * 128 + col, s4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x16 a = acc[i][j];
+                    epi_put4(wl, 32 * j + (lane & 31), col, (a[4 * g] * sam[j]) * s4[0],
+                             (a[4 * g + 1] * sam[j]) * s4[1], (a[4 * g + 2] * sam[j]) * s4[2],
+                             (a[4 * g + 3] * sam[j]) * s4[3]);
+                }
+            }
+        __syncthreads();
+        epi_store(wl, (uint16_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
+        return;
+    }
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -586,6 +755,175 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
             }
     }
 }
+
+// ---------------------------------------------------------------------------
+// Block-wise scaled GEMM for M > 32 on the FP8 matrix cores:
+//   y[m, n] = sum_kb s_a[m, kb] * s_w[n / 128, kb] * P_kb[m, n],
+// with P_kb the 128-deep partial product of k block kb (FP8 Inference
+// Explained, in depth -- "Inside a quantized linear layer": scales that vary
+// along k cannot leave the sum; Quantization: FP8 inference and KV-cache
+// quantization -- "Training in FP8 or lower": each 128-element partial sum
+// moves to fp32 with its scales).  A k block is exactly one
+// v_mfma_f32_16x16x128_f8f6f4 per 16 x 16 fragment, started from zero; the
+// result is multiplied by the fragment's scale product and added to an fp32
+// accumulator with vector FMAs, so the accumulators live in the vector
+// registers the FMAs can address.
+//
+// 256 x 256 tile per workgroup of 8 waves (two per SIMD).  Wave (wm, wn) =
+// (wave % 4, wave / 4) owns tile rows 64 wm .. 64 wm + 63 and columns
+// 128 wn .. 128 wn + 127: 4 A fragments x 8 W fragments, 128 accumulator
+// registers.  It holds its 4 A fragments and streams the 8 W fragments from
+// LDS two at a time, which keeps the wave within 256 registers.
+//
+// Staging as in the per-token kernels (direct global-to-LDS copies in fragment
+// order, two stages, copies two k blocks ahead, fence-free barriers), with
+// the copies split by operand: waves 0-3 copy the A tile, waves 4-7 the W
+// tile, 8 one-kilobyte copies each.  Each wave also copies one 4-byte value
+// per lane of the block's scales: waves 0-3 the s_a of tile rows 64 w + lane,
+// waves 4-7 the s_w of the tile's two 128-column blocks (lane % 2), so every
+// wave has 9 copies per stage.  A stage is refilled once every wave has read
+// all of it (the W fragments are read until the last row of multiplies).
+constexpr int kBwOps = 32 * kPackBlock;       // A 32 KB + W 32 KB
+constexpr int kBwStage = kBwOps + 2048;       // + s_a (256 floats) + s_w (4 x 64 floats)
+constexpr int kBwCopies = 9;                  // copies per wave per stage
+
+__device__ __forceinline__ void copy4_to_lds(const float* src, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off"
+        :
+        : "s"(lds_addr), "v"(src)
+        : "memory", "m0");
+}
+
+template <bool kYbf16, bool kWPacked, bool kAPacked>
+__global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __restrict__ A,
+                                                             const float* __restrict__ sa,
+                                                             const uint8_t* __restrict__ W,
+                                                             const float* __restrict__ sw, void* __restrict__ Y,
+                                                             int M, int N, int K, int tiles_per_xcd) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages of kBwStage
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 3, wn = wave >> 2;
+    int tile;
+    int64_t m_base, n_base;
+    tile_coords(M, N, tiles_per_xcd, tile, m_base, n_base);
+    if (tile < 0) return;
+    const int nkb = K >> 7;
+    const int64_t nbw = ((int64_t)N + 127) >> 7;
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // this wave's copies: 8 kilobytes of one operand tile and 256 bytes of scales
+    const bool cp_a = wave < 4;
+    uint32_t o[8];
+    if (cp_a) tile_copy_offsets<kAPacked>(o, m_base, M, K, wave & 3, lane);
+    else tile_copy_offsets<kWPacked>(o, n_base, N, K, wave & 3, lane);
+    const uint8_t* src = cp_a ? (kAPacked ? A + (m_base >> 4) * (int64_t)nkb * kPackBlock : A + m_base * K)
+                              : (kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K);
+    const int64_t src_kb = cp_a ? (kAPacked ? kPackBlock : 128) : (kWPacked ? kPackBlock : 128);
+    const uint32_t dst_op = cp_a ? 0u : (uint32_t)(16 * kPackBlock);
+    const float* ssrc;
+    if (cp_a) {
+        int64_t m = m_base + 64 * wave + lane;
+        m = m < M ? m : M - 1;
+        ssrc = sa + m * nkb;
+    } else {
+        int64_t nb = (n_base >> 7) + (lane & 1);
+        nb = nb < nbw ? nb : nbw - 1;
+        ssrc = sw + nb * nkb;
+    }
+    const uint32_t dst_sc = (uint32_t)(kBwOps + 256 * wave);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+
+    // copy c (0..8) of block kb into the stage at LDS address `stage`
+    auto issue_copy = [&](int c, uint32_t stage, int kb) __attribute__((always_inline)) {
+        if (c < 8) {
+            const int q = (wave & 3) * 8 + c, j = q >> 1, h = q & 1;
+            copy16_to_lds(src + (int64_t)kb * src_kb + o[c], stage + dst_op + (uint32_t)(j * kPackBlock + h * 1024));
+        } else {
+            copy4_to_lds(ssrc + kb, stage + dst_sc);
+        }
+    };
+
+    if (nkb > 0) {
+        const int b1 = nkb > 1 ? 1 : 0;
+#pragma unroll
+        for (int c = 0; c < kBwCopies; ++c) issue_copy(c, lds0, 0);
+#pragma unroll
+        for (int c = 0; c < kBwCopies; ++c) issue_copy(c, lds0 + kBwStage, b1);
+    }
+    for (int kb = 0; kb < nkb; ++kb) {
+        const uint32_t cur_lds = lds0 + (uint32_t)((kb & 1) * kBwStage);
+        const uint8_t* cur = smem + (kb & 1) * kBwStage;
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(kBwCopies));  // this wave's copies of block kb have landed
+        barrier_no_fence();                                 // ... and every other wave's
+        const float* ls = reinterpret_cast<const float*>(cur + kBwOps);
+        const float swv = ls[256 + wn];
+        float f[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = ls[64 * wm + 16 * j + (lane & 15)] * swv;
+        Frag af[4], wf[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) af[j] = load_frag_packed(cur + (4 * wm + j) * kPackBlock, lane);
+        const uint8_t* lw = cur + (16 + 8 * wn) * kPackBlock;
+        wf[0] = load_frag_packed(lw, lane);
+        const int nxt = kb + 2 < nkb ? kb + 2 : nkb - 1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < 7) {
+                wf[(i + 1) & 1] = load_frag_packed(lw + (i + 1) * kPackBlock, lane);
+            } else {
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the stage are done
+                barrier_no_fence();                  // ... and every other wave's: refill it with block kb + 2
+#pragma unroll
+                for (int c = 0; c < kBwCopies; ++c) issue_copy(c, cur_lds, nxt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 p = mma_fp8(wf[i & 1], af[j], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], f[j], acc[i][j][r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
+
+    if (kYbf16) {
+        __syncthreads();  // every wave is done with the stages: the LDS now holds the output tiles
+        uint8_t* wl = smem + wave * (kEpiWaveBytes / 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 a = acc[i][j];
+                epi_put4(wl, 16 * j + (lane & 15), 16 * i + 4 * (lane >> 4), a[0], a[1], a[2], a[3]);
+            }
+        __syncthreads();
+        epi_store<64>(wl, (uint16_t*)Y, M, N, m_base + wm * 64, n_base + wn * 128, lane);
+        return;
+    }
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t m = m_base + wm * 64 + 16 * j + (lane & 15);
+        if (m >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t n0 = n_base + wn * 128 + 16 * i + 4 * (lane >> 4);
+            if (n0 < N) store4_raw<kYbf16>(Y, N, m, n0, acc[i][j], vec_ok);
+        }
+    }
+}
+static_assert(8 * (kEpiWaveBytes / 2) <= 2 * kBwStage, "the staged output reuses the two operand stages");
 
 template <bool kFp8, bool kYbf16, bool kWPacked, bool kAPacked, int kMT, int kNS, int kKS, int kDepth>
 static void launch_skinny(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw, void* y,
@@ -644,6 +982,52 @@ hipError_t launch_gemm(const uint8_t* aq, bool a_packed, const float* a_scales, 
     const int m = (int)M, n = (int)N, k = (int)K;
     if (fp8_mfma) return launch_gemm_m<true>(aq, a_packed, a_scales, pt, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
     return launch_gemm_m<false>(aq, a_packed, a_scales, pt, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
+}
+
+template <bool kFp8, bool kYbf16, bool kWPacked, bool kAPacked>
+static hipError_t launch_blockwise_t(const uint8_t* aq, const float* sa, const uint8_t* wq, const float* sw, void* y,
+                                     int M, int N, int K, hipStream_t stream) {
+    dim3 block(64 * SKINNY_KS);
+    dim3 grid((unsigned)((N + 16 * SKINNY_NS - 1) / (16 * SKINNY_NS)));
+    if (M <= 16) {
+        gemm_skinny<kFp8, kYbf16, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
+            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K);
+    } else if (M <= 32) {
+        gemm_skinny<kFp8, kYbf16, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
+            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K);
+    } else if (kFp8) {
+        const int tiles = ((M + kBig - 1) / kBig) * ((N + kBig - 1) / kBig);
+        const int per = (tiles + 7) / 8;
+        gemm_big_blockwise<kYbf16, kWPacked, kAPacked>
+            <<<dim3((unsigned)(per * 8)), dim3(512), 2 * kBwStage, stream>>>(aq, sa, wq, sw, y, M, N, K, per);
+    } else {
+        return hipErrorInvalidValue;  // exact block-wise accumulation exists for M <= 32 only (checked by the ABI)
+    }
+    return hipGetLastError();
+}
+
+template <bool kFp8>
+static hipError_t launch_blockwise_m(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq,
+                                     bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
+                                     hipStream_t stream) {
+#define FP8SG_BW(YB, WP, AP) launch_blockwise_t<kFp8, YB, WP, AP>(aq, sa, wq, sw, y, M, N, K, stream)
+    if (y_bf16) {
+        if (a_packed) return w_packed ? FP8SG_BW(true, true, true) : FP8SG_BW(true, false, true);
+        return w_packed ? FP8SG_BW(true, true, false) : FP8SG_BW(true, false, false);
+    }
+    if (a_packed) return w_packed ? FP8SG_BW(false, true, true) : FP8SG_BW(false, false, true);
+    return w_packed ? FP8SG_BW(false, true, false) : FP8SG_BW(false, false, false);
+#undef FP8SG_BW
+}
+
+hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* a_scales, const uint8_t* wq,
+                                 bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N,
+                                 int64_t K, bool fp8_mfma, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    const int m = (int)M, n = (int)N, k = (int)K;
+    if (fp8_mfma)
+        return launch_blockwise_m<true>(aq, a_packed, a_scales, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
+    return launch_blockwise_m<false>(aq, a_packed, a_scales, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -12,6 +12,13 @@ namespace fp8sg {
 hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
                             bool packed, hipStream_t stream);
 
+// Block-wise dynamic quantization: activations in 1 x 128 groups (scales [M, K/128]),
+// weights in 128 x 128 blocks (scales [ceil(N/128), K/128]); K % 128 == 0.
+hipError_t launch_group_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
+                              bool packed, hipStream_t stream);
+hipError_t launch_block_quant_weight(const void* w, bool w_is_bf16, int64_t N, int64_t K, uint8_t* q, float* scales,
+                                     hipStream_t stream);
+
 // Static per-tensor E4M3 quantization of [M, K] (K % 128 == 0) into the fragment order.
 hipError_t launch_static_quant_packed(const void* x, bool x_is_bf16, int64_t M, int64_t K, const float* scale,
                                       uint8_t* q, hipStream_t stream);
@@ -22,6 +29,11 @@ hipError_t launch_grouped_quant(const void* x, bool x_is_bf16, int64_t numel, co
 hipError_t launch_gemm(const uint8_t* aq, bool a_packed, const float* a_scales, bool a_per_token, const uint8_t* wq,
                        bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
                        bool fp8_mfma, hipStream_t stream);
+
+// Block-wise scaled GEMM: a_scales [M, K/128], w_scales [ceil(N/128), K/128].
+hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* a_scales, const uint8_t* wq,
+                                 bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N,
+                                 int64_t K, bool fp8_mfma, hipStream_t stream);
 
 hipError_t launch_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, hipStream_t stream);
 

@@ -5,6 +5,10 @@
 //    between the absolute-maximum reduction and the encode, so X is read from
 //    HBM once (FP8 Inference Explained, in depth -- "Inside a quantized linear
 //    layer": find each token's amax, divide, cast to E4M3).
+//  * group_quant / block_quant_weight: the block-wise variant -- one dynamic
+//    scale per token and 128-element group along k for activations, one per
+//    128 x 128 block for weights (FP8 Quantization notebook -- "Granularity";
+//    FP8 Inference Explained, in depth -- "Scales and their granularity").
 //  * grouped_quant: given scales, one per group of `inner` consecutive
 //    elements, cycling over `nscales` groups (static per-tensor: one group;
 //    KV cache [B,S,H,D]: inner = D, nscales = H).  Saturating (Quantization: FP8
@@ -148,6 +152,103 @@ hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K,
                       : launch_row_quant_t<uint16_t, false>((const uint16_t*)x, M, K, q, scales, stream);
     return packed ? launch_row_quant_t<float, true>((const float*)x, M, K, q, scales, stream)
                   : launch_row_quant_t<float, false>((const float*)x, M, K, q, scales, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Block-wise dynamic quantization.
+//
+// Activations, one scale per (row, 128-element group): a group is 16 chunks of
+// 8 elements, one chunk per thread, so the 16 threads of a group take its
+// maximum with four shuffles and each encodes its own chunk.  The grid strides
+// over chunks in multiples of 16 and the chunk count is a multiple of 16
+// (K % 128 == 0), so a group's 16 threads are always active together.
+// scales[m * (K / 128) + g] = RN32(amax / 448) (1.0 for an all-zero group).
+template <typename InT, bool kPacked>
+__global__ __launch_bounds__(256) void group_quant(const InT* __restrict__ x, int64_t K, int64_t nchunks,
+                                                   uint8_t* __restrict__ q, float* __restrict__ scales) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
+        float v[8];
+        load_chunk<InT>(x + c * 8, v);
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+        const float s = dynamic_scale(amax, kE4M3Max);
+        if ((c & 15) == 0) scales[c >> 4] = s;
+        const QScale p = make_qscale(s, kE4M3Max);
+        uint8_t* dst;
+        if (kPacked) {
+            const int64_t e = c * 8, m = e / K;
+            dst = q + packed_offset(m, e - m * K, K >> 7);
+        } else {
+            dst = q + c * 8;
+        }
+        *reinterpret_cast<uint2*>(dst) = encode_chunk_dynamic<InT>(v, p);
+    }
+}
+
+hipError_t launch_group_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
+                              bool packed, hipStream_t stream) {
+    const int64_t nchunks = M * (K / 8);
+    if (nchunks == 0) return hipSuccess;
+    int64_t blocks = (nchunks + 255) / 256;
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    dim3 grid((unsigned)blocks), block(256);
+    if (x_is_bf16) {
+        if (packed) group_quant<uint16_t, true><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nchunks, q, scales);
+        else group_quant<uint16_t, false><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nchunks, q, scales);
+    } else {
+        if (packed) group_quant<float, true><<<grid, block, 0, stream>>>((const float*)x, K, nchunks, q, scales);
+        else group_quant<float, false><<<grid, block, 0, stream>>>((const float*)x, K, nchunks, q, scales);
+    }
+    return hipGetLastError();
+}
+
+// Weights, one scale per 128 x 128 block (the last row block is short when
+// N % 128 != 0).  One workgroup per block: thread t holds chunk t % 16 of rows
+// t / 16 + 16 i, i < 8, in registers between the block maximum and the encode.
+// scales[(n / 128) * (K / 128) + k / 128].
+template <typename InT>
+__global__ __launch_bounds__(256) void block_quant_weight(const InT* __restrict__ w, int64_t N, int64_t K, int nkb,
+                                                          uint8_t* __restrict__ q, float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int64_t blk = blockIdx.x;
+    const int64_t nb = blk / nkb;
+    const int64_t col = (blk - nb * nkb) * 128 + (threadIdx.x & 15) * 8;
+    float v[8][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = nb * 128 + (threadIdx.x >> 4) + 16 * i;
+        if (row < N) {
+            load_chunk<InT>(w + row * K + col, v[i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(v[i][j]));
+        }
+    }
+    amax = block_max(amax, red);
+    const float s = dynamic_scale(amax, kE4M3Max);
+    if (threadIdx.x == 0) scales[blk] = s;
+    const QScale p = make_qscale(s, kE4M3Max);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = nb * 128 + (threadIdx.x >> 4) + 16 * i;
+        if (row < N) *reinterpret_cast<uint2*>(q + row * K + col) = encode_chunk_dynamic<InT>(v[i], p);
+    }
+}
+
+hipError_t launch_block_quant_weight(const void* w, bool w_is_bf16, int64_t N, int64_t K, uint8_t* q, float* scales,
+                                     hipStream_t stream) {
+    const int64_t nkb = K / 128, nbw = (N + 127) / 128;
+    if (nkb == 0 || nbw == 0) return hipSuccess;
+    dim3 grid((unsigned)(nkb * nbw)), block(256);
+    if (w_is_bf16)
+        block_quant_weight<uint16_t><<<grid, block, 0, stream>>>((const uint16_t*)w, N, K, (int)nkb, q, scales);
+    else
+        block_quant_weight<float><<<grid, block, 0, stream>>>((const float*)w, N, K, (int)nkb, q, scales);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -64,6 +64,13 @@ def check_outputs(y_bits, acc_gpu, aq_rows, sa_rows, wq_rows, sw_rows, accum, wh
     bad = err > bound
     assert not bad.any(), (f"{what}: accumulator outside tolerance at {int(bad.sum())} outputs; "
                            f"worst err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}")
+    # the bf16 epilogue of the same accumulator: y = bf16_rne(RN32(RN32(acc * s_a) * s_w)), bit for bit
+    # (the fp32 output with unit scales shares the bf16 kernel's main loop, so acc_gpu is its accumulator)
+    sa32 = np.asarray(sa_rows, np.float32).reshape(-1, 1)
+    sw32 = np.asarray(sw_rows, np.float32).reshape(1, -1)
+    y_epi = fp8.bf16_round_bits(((acc_gpu.astype(np.float32) * sa32) * sw32).astype(np.float64))
+    mism = y_epi != y_bits
+    assert not mism.any(), f"{what}: {int(mism.sum())} bf16 outputs differ from the scaled accumulator"
     if accum != "exact":
         return
     y_ref_bits = fp8.bf16_round_bits(w8a8.scaled_gemm_f64(acc, sa_rows, sw_rows))
