@@ -200,6 +200,62 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block-wise dynamic activation quantization: one scale per token and group of
+ * 128 consecutive k, so an outlier widens the step of its own group only (FP8
+ * Quantization notebook -- "Granularity"; FP8 Inference Explained, in depth --
+ * "Scales and their granularity").  Each group's maximum lands on 448.
+ *   x       [M, K] input, x_dtype FP8SG_BF16 or FP8SG_F32
+ *   q       E4M3 codes (output): [M, K] row-major when layout is 0; with
+ *           FP8SG_A_PACKED the fragment order of fp8_pack_weights
+ *           (fp8_packed_weight_bytes(M, K) bytes; the padding rows of the last
+ *           16-row tile are left unwritten)
+ *   scales  [M, K / 128] fp32 (output), row-major:
+ *           s[m, g] = RN32(max_{k in group g} |x[m, k]| / 448), or 1.0 when 0
+ *   layout  0 or FP8SG_A_PACKED; other bits: FP8SG_E_DTYPE
+ *   K % 128 == 0.
+ */
+fp8sg_status fp8_quant_per_token_group(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* q,
+                                       float* scales, int layout, void* stream);
+
+/*
+ * Offline block-wise weight quantization: one scale per 128 x 128 block of W
+ * (FP8 Quantization notebook -- "Granularity": per-block scaling of weights).
+ *   w         [N, K] FP8SG_F32 or FP8SG_BF16
+ *   wq        [N, K] E4M3 codes (output)
+ *   w_scales  [ceil(N / 128), K / 128] fp32 (output), row-major:
+ *             s[b, g] = RN32(max |W[128 b .. 128 b + 127, 128 g .. 128 g + 127]| / 448),
+ *             or 1.0 when 0; the last row block is short when N % 128 != 0
+ *   K % 128 == 0.
+ */
+fp8sg_status fp8_quant_weight_blockwise(const void* w, int w_dtype, int64_t N, int64_t K, uint8_t* wq,
+                                        float* w_scales, void* stream);
+
+/*
+ * Block-wise scaled GEMM.  The scales vary along k, so each 128-deep partial
+ * product P_g is scaled on its own before the partials are summed in fp32
+ * (FP8 Inference Explained, in depth -- "Inside a quantized linear layer", on
+ * why finer-than-channel scales need a purpose-built GEMM; Quantization: FP8
+ * inference and KV-cache quantization -- "Training in FP8 or lower", on
+ * moving each 128-element partial sum to FP32):
+ *   y[m, n] = sum_g s_a[m, g] * s_w[n / 128, g] * P_g[m, n],
+ *   P_g[m, n] = sum_{k = 128 g}^{128 g + 127} a_q[m, k] * w_q[n, k].
+ *   a_q       [M, K] E4M3 codes (row-major, or FP8SG_A_PACKED fragment order)
+ *   a_scales  [M, K / 128] fp32, as written by fp8_quant_per_token_group
+ *   wq        [N, K] E4M3 codes (row-major, or FP8SG_W_PACKED fragment order)
+ *   w_scales  [ceil(N / 128), K / 128] fp32, as written by fp8_quant_weight_blockwise
+ *   y         [M, N] FP8SG_BF16 (y rounded to nearest even) or FP8SG_F32 (y)
+ *   layout    0 or an OR of FP8SG_W_PACKED and FP8SG_A_PACKED
+ *   accum     FP8SG_ACCUM_MFMA_FP8: each P_g is one FP8 matrix-core product
+ *             (with that hardware's in-instruction alignment, see fp8sg_accum);
+ *             FP8SG_ACCUM_EXACT: P_g formed exactly on the bf16 matrix cores,
+ *             available for M <= 32 only (larger M: FP8SG_E_DTYPE).
+ *   K % 128 == 0; M, N >= 0 arbitrary.
+ */
+fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales, const uint8_t* wq, int layout,
+                                       const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N,
+                                       int64_t K, int accum, void* stream);
+
+/*
  * KV-cache calibration: one scale per kv head, s_h = RN32(amax_h / max) over
  * all (b, s, d) of head h, or 1.0 when that is 0 (per-head KV scales require
  * calibration -- Quantization: FP8 inference and KV-cache quantization,

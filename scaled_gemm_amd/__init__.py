@@ -15,6 +15,7 @@ from .fp8sg import (  # noqa: F401
     Fp8sgError,
     SCALE_PER_TENSOR,
     SCALE_PER_TOKEN,
+    A_PACKED,
     W_PACKED,
     W_ROW_MAJOR,
     declared_symbols,
@@ -25,9 +26,12 @@ from .fp8sg import (  # noqa: F401
     fp8_pack_weights,
     fp8_packed_weight_bytes,
     fp8_quant_per_tensor_static,
+    fp8_quant_per_token_group,
+    fp8_quant_weight_blockwise,
     fp8_quant_per_token,
     fp8_quant_weight_per_channel,
     fp8_scaled_gemm,
+    fp8_scaled_gemm_blockwise,
     fp8_scaled_gemm_workspace_size,
     lib,
     status_string,

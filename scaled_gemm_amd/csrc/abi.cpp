@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -203,6 +203,56 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
     const bool a_packed = quantize_here ? pack_here : (layout & FP8SG_A_PACKED) != 0;
     return launched(fp8sg::launch_gemm(aq, a_packed, sa, per_token, wq, (layout & FP8SG_W_PACKED) != 0, w_scales, y,
                                        y_dtype == FP8SG_BF16, M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, s));
+}
+
+fp8sg_status fp8_quant_per_token_group(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* q, float* scales,
+                                       int layout, void* stream) {
+    if (!is_hp(x_dtype)) return FP8SG_E_DTYPE;
+    if (layout != 0 && layout != FP8SG_A_PACKED) return FP8SG_E_DTYPE;
+    if (M < 0 || K < 0 || M >= kMaxDim || K >= kMaxDim || K % 128 != 0) return FP8SG_E_SHAPE;
+    if (M == 0 || K == 0) return FP8SG_OK;
+    if (!x || !q || !scales) return FP8SG_E_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    return launched(fp8sg::launch_group_quant(x, x_dtype == FP8SG_BF16, M, K, q, scales, layout == FP8SG_A_PACKED,
+                                              (hipStream_t)stream));
+}
+
+fp8sg_status fp8_quant_weight_blockwise(const void* w, int w_dtype, int64_t N, int64_t K, uint8_t* wq,
+                                        float* w_scales, void* stream) {
+    if (!is_hp(w_dtype)) return FP8SG_E_DTYPE;
+    if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim || K % 128 != 0) return FP8SG_E_SHAPE;
+    if (N == 0 || K == 0) return FP8SG_OK;
+    if ((N + 127) / 128 * (K / 128) >= kMaxDim) return FP8SG_E_SHAPE;  // one workgroup per block
+    if (!w || !wq || !w_scales) return FP8SG_E_NULL;
+    if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(w_scales, 4)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    return launched(fp8sg::launch_block_quant_weight(w, w_dtype == FP8SG_BF16, N, K, wq, w_scales,
+                                                     (hipStream_t)stream));
+}
+
+fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales, const uint8_t* wq, int layout,
+                                       const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                       int accum, void* stream) {
+    if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
+    if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
+    if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED)) != 0) return FP8SG_E_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (K % 128 != 0) return FP8SG_E_SHAPE;
+    if (accum == FP8SG_ACCUM_EXACT && M > 32) return FP8SG_E_DTYPE;  // exact partials: skinny kernel only
+    if (M == 0 || N == 0) return FP8SG_OK;
+    if (!y) return FP8SG_E_NULL;
+    if (K > 0 && (!a_q || !wq || !a_scales || !w_scales)) return FP8SG_E_NULL;
+    if ((a_q && !aligned(a_q, 16)) || (wq && !aligned(wq, 16)) || !aligned(y, 16)) return FP8SG_E_ALIGN;
+    if ((a_scales && !aligned(a_scales, 4)) || (w_scales && !aligned(w_scales, 4))) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    // K == 0 launches too: the kernels read no scale and write the empty sums (zeros)
+    return launched(fp8sg::launch_gemm_blockwise(a_q, (layout & FP8SG_A_PACKED) != 0, a_scales, wq,
+                                                 (layout & FP8SG_W_PACKED) != 0, w_scales, y, y_dtype == FP8SG_BF16,
+                                                 M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, (hipStream_t)stream));
 }
 
 fp8sg_status fp8_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,

@@ -57,6 +57,9 @@ _SIGS = {
     "fp8_pack_weights": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _sz,
                                _vp]),
+    "fp8_quant_per_token_group": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]),
+    "fp8_quant_weight_blockwise": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_scaled_gemm_blockwise": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
     "fp8_kv_calibrate": (_i32, [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp]),
     "fp8_kv_quant": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
     "fp8_kv_dequant": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
@@ -232,6 +235,71 @@ def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch
     _check(lib().fp8_scaled_gemm(_ptr(a), a_code, _ptr(a_scales), mode, _ptr(wq), layout, _ptr(w_scales), _ptr(y),
                                  y_code, M, N, K, _ACCUM[accum], _ptr(workspace), ws_bytes, _stream(stream)),
            "fp8_scaled_gemm")
+    return y
+
+
+def fp8_quant_per_token_group(x: torch.Tensor, layout="row_major", q: Optional[torch.Tensor] = None,
+                              scales: Optional[torch.Tensor] = None, stream=None):
+    """x [M, K] (bf16/fp32) -> (codes, scales [M, K / 128] fp32): one scale per
+    token and 128-element group.  layout="packed": the codes in the fragment
+    order (1-D, fp8_packed_weight_bytes(M, K) bytes)."""
+    _need(x, "x", _HP)
+    M, K = x.shape
+    packed = _LAYOUT[layout] == W_PACKED
+    qshape = (fp8_packed_weight_bytes(M, K),) if packed else (M, K)
+    q = torch.empty(qshape, dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if scales is None else scales
+    _need(q, "q", (torch.uint8,), qshape)
+    _need(scales, "scales", (torch.float32,), (M, K // 128))
+    _check(lib().fp8_quant_per_token_group(_ptr(x), _hp_code(x), M, K, _ptr(q), _ptr(scales),
+                                           A_PACKED if packed else 0, _stream(stream)), "fp8_quant_per_token_group")
+    return q, scales
+
+
+def fp8_quant_weight_blockwise(w: torch.Tensor, wq: Optional[torch.Tensor] = None,
+                               w_scales: Optional[torch.Tensor] = None, stream=None):
+    """w [N, K] (fp32/bf16) -> (wq [N, K] uint8, w_scales [ceil(N/128), K/128] fp32)."""
+    _need(w, "w", _HP)
+    N, K = w.shape
+    sshape = ((N + 127) // 128, K // 128)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=w.device) if wq is None else wq
+    w_scales = torch.empty(sshape, dtype=torch.float32, device=w.device) if w_scales is None else w_scales
+    _need(wq, "wq", (torch.uint8,), (N, K))
+    _need(w_scales, "w_scales", (torch.float32,), sshape)
+    _check(lib().fp8_quant_weight_blockwise(_ptr(w), _hp_code(w), N, K, _ptr(wq), _ptr(w_scales), _stream(stream)),
+           "fp8_quant_weight_blockwise")
+    return wq, w_scales
+
+
+def fp8_scaled_gemm_blockwise(a: torch.Tensor, a_scales: torch.Tensor, wq: torch.Tensor, w_scales: torch.Tensor, *,
+                              out_dtype=torch.bfloat16, accum="mfma_fp8", w_layout="row_major", a_layout="row_major",
+                              a_shape: Optional[tuple] = None, w_shape: Optional[tuple] = None,
+                              y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y [M, N] = sum_g diag(s_a[:, g]) (A_q W_q^T)_g diag(s_w[n // 128, g]).
+
+    a: E4M3 codes [M, K] (or the packed 1-D buffer with a_shape=(M, K));
+    a_scales [M, K/128]; wq [N, K] (or packed with w_shape=(N, K));
+    w_scales [ceil(N/128), K/128].  accum="exact" needs M <= 32."""
+    _need(a, "a", (torch.uint8,))
+    _need(wq, "wq", (torch.uint8,))
+    a_packed = _LAYOUT[a_layout] == W_PACKED
+    w_packed = _LAYOUT[w_layout] == W_PACKED
+    M, K = (int(v) for v in a_shape) if a_packed else a.shape
+    N = int(w_shape[0]) if w_packed else wq.shape[0]
+    if a_packed and a.numel() != fp8_packed_weight_bytes(M, K):
+        raise ValueError(f"packed a has {a.numel()} bytes, expected {fp8_packed_weight_bytes(M, K)}")
+    if w_packed and (w_shape is None or int(w_shape[1]) != K or wq.numel() != fp8_packed_weight_bytes(N, K)):
+        raise ValueError("w_layout='packed' takes w_shape=(N, K) and fp8_packed_weight_bytes(N, K) bytes")
+    if not w_packed and wq.shape[1] != K:
+        raise ValueError(f"wq has shape {tuple(wq.shape)}, expected K = {K}")
+    _need(a_scales, "a_scales", (torch.float32,), (M, K // 128))
+    _need(w_scales, "w_scales", (torch.float32,), ((N + 127) // 128, K // 128))
+    y_code = {torch.bfloat16: BF16, torch.float32: F32}[out_dtype]
+    y = torch.empty((M, N), dtype=out_dtype, device=a.device) if y is None else y
+    _need(y, "y", (out_dtype,), (M, N))
+    layout = (W_PACKED if w_packed else 0) | (A_PACKED if a_packed else 0)
+    _check(lib().fp8_scaled_gemm_blockwise(_ptr(a), _ptr(a_scales), _ptr(wq), layout, _ptr(w_scales), _ptr(y), y_code,
+                                           M, N, K, _ACCUM[accum], _stream(stream)), "fp8_scaled_gemm_blockwise")
     return y
 
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     names = sg.declared_symbols()
-    assert len(names) == 13
+    assert len(names) == 16
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
     missing = [n for n in names if n not in exported]
@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert sg.lib().fp8sg_version() == 3
+    assert sg.lib().fp8sg_version() == 4
     for st in range(8):
         assert sg.status_string(st)
     assert sg.status_string(99) == "unknown status"
@@ -47,6 +47,30 @@ def lib():
 
 
 A = 4096  # a 16-byte-aligned fake device address: never dereferenced, validation fails first
+
+
+def test_blockwise_validation(lib):
+    # group quantizer: K % 128, dtype, layout bits, nulls, alignment, empty work
+    assert lib.fp8_quant_per_token_group(A, b.BF16, 4, 64, A, A, 0, None) == b.E_SHAPE
+    assert lib.fp8_quant_per_token_group(A, b.E4M3, 4, 128, A, A, 0, None) == b.E_DTYPE
+    assert lib.fp8_quant_per_token_group(A, b.BF16, 4, 128, A, A, b.W_PACKED, None) == b.E_DTYPE
+    assert lib.fp8_quant_per_token_group(A, b.BF16, 4, 128, A, None, 0, None) == b.E_NULL
+    assert lib.fp8_quant_per_token_group(A + 4, b.BF16, 4, 128, A, A, 0, None) == b.E_ALIGN
+    assert lib.fp8_quant_per_token_group(None, b.BF16, 0, 128, None, None, 0, None) == b.OK
+    # weight blocks
+    assert lib.fp8_quant_weight_blockwise(A, b.F32, 4, 100, A, A, None) == b.E_SHAPE
+    assert lib.fp8_quant_weight_blockwise(A, b.E5M2, 4, 128, A, A, None) == b.E_DTYPE
+    assert lib.fp8_quant_weight_blockwise(A, b.F32, 4, 128, None, A, None) == b.E_NULL
+    assert lib.fp8_quant_weight_blockwise(None, b.F32, 0, 128, None, None, None) == b.OK
+    # GEMM: exact accumulation only for M <= 32; K % 128; layout bits; nulls; alignment
+    g = lib.fp8_scaled_gemm_blockwise
+    assert g(A, A, A, 0, A, A, b.BF16, 33, 8, 128, b.ACCUM_EXACT, None) == b.E_DTYPE
+    assert g(A, A, A, 0, A, A, b.BF16, 4, 8, 100, b.ACCUM_MFMA_FP8, None) == b.E_SHAPE
+    assert g(A, A, A, 4, A, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_DTYPE
+    assert g(A, A, A, 0, A, A, b.E4M3, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_DTYPE
+    assert g(A, None, A, 0, A, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_NULL
+    assert g(A, A, A, 0, A + 2, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_ALIGN
+    assert g(None, None, None, 0, None, None, b.BF16, 0, 8, 128, b.ACCUM_MFMA_FP8, None) == b.OK
 
 
 def test_quant_validation(lib):

@@ -1,0 +1,217 @@
+"""GPU parity of the block-wise scaled FP8 path (1 x 128 activation groups,
+128 x 128 weight blocks) against the CPU oracle (oracle/blockwise.py), through
+the C ABI.
+
+Quantizers: codes and scales bit-exact.
+
+GEMM, y = sum_g s_a[m, g] s_w[n // 128, g] P_g (read through the fp32 output):
+  * exact mode (bf16 matrix cores, M <= 32): |y - y_exact| <= 1e-5 * T, with
+    T = sum_g |s_a s_w| sum_{k in g} |a_k w_k| -- the accumulator tolerance of
+    the per-token GEMM applied to the block-scaled terms;
+  * FP8 matrix-core mode: the bound derived from that hardware's summation
+    (inside each 8-product group, truncation below 2^(e_max - 13), so a group
+    loses less than 7 * 2^(e_max - 13)), scaled per block, plus one float32
+    rounding per block partial, scale product and accumulation:
+    |y - y_exact| <= sum_g |s_a s_w| sum_{groups in g} 7 * 2^(e_max - 13) + (G + 3) * 2^-24 * T.
+The bf16 output must equal bf16_rne(fp32 output) bit for bit (same kernel,
+same accumulator), and in exact mode lie within one bf16 ulp of the correctly
+rounded exact value (outside that only where the tolerance itself exceeds an
+ulp).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_codes_equal, dev, dev_bf16, host, host_bits16, require_gpu
+from oracle import blockwise as bw
+from oracle import fp8
+from workloads import bf16_bits_from_f32, decode_inputs, f32_from_bf16_bits, prefill_inputs, tiny_w8a8
+
+pytestmark = pytest.mark.gpu
+
+import scaled_gemm_amd as sg  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def bf16_ulp(y):
+    a = np.abs(y)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.exp2(np.maximum(e, -126) - 7)
+
+
+def pack_reference(q):
+    from test_abi_host import pack_reference as pr
+    return pr(q)
+
+
+def fp8_group_loss(a_rows, w_cols):
+    """[r, c] sum over the 8-product groups of 7 * 2^(e_max - 13), per 128-deep block: [G, r, c]."""
+    a = fp8.decode(a_rows)
+    w = fp8.decode(w_cols)
+    K = a.shape[1]
+    G = K // 128
+    out = np.zeros((G, a.shape[0], w.shape[0]))
+    for i in range(a.shape[0]):
+        p = np.abs(a[i][None, :] * w)                       # [c, K] exact products
+        g = p.reshape(w.shape[0], K // 8, 8).max(axis=-1)    # [c, K / 8]
+        e = np.floor(np.log2(np.where(g > 0, g, 1.0)))
+        loss = np.where(g > 0, 7.0 * np.exp2(e - 13), 0.0)  # [c, K / 8]
+        out[:, i, :] = loss.reshape(w.shape[0], G, 16).sum(axis=-1).T
+    return out
+
+
+def check_gemm(y_f32, y_bits, aq, sa, wq, sw, cols, accum, what):
+    """aq/sa: the sampled rows; wq: all rows of W (for the block scales); cols: sampled columns."""
+    sw_cols = sw                      # [NB, G]; indexed by column block below
+    wq_c = wq[cols]
+    # the oracle on the sampled columns: column n uses block n // 128 of s_w
+    sw_rows = np.repeat(sw_cols, 128, axis=0)[cols]          # [c, G] scale of each sampled column
+    P = bw.blockwise_partials(aq, wq_c)                       # [G, r, c] exact
+    scale = sa.astype(np.float64).T[:, :, None] * sw_rows.astype(np.float64).T[:, None, :]  # [G, r, c]
+    y_exact = (scale * P).sum(axis=0)
+    a = np.abs(fp8.decode(aq))
+    w = np.abs(fp8.decode(wq_c))
+    G = aq.shape[1] // 128
+    T = sum(np.abs(scale[g]) * (a[:, 128 * g:128 * g + 128] @ w[:, 128 * g:128 * g + 128].T) for g in range(G))
+    err = np.abs(y_f32.astype(np.float64) - y_exact)
+    if accum == "exact":
+        bound = 1e-5 * T
+    else:
+        bound = (np.abs(scale) * fp8_group_loss(aq, wq_c)).sum(axis=0) + (G + 3) * 2.0 ** -24 * T
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} outputs outside the bound; "
+                           f"worst err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}")
+    same = fp8.bf16_round_bits(y_f32.astype(np.float64)) == y_bits
+    assert same.all(), f"{what}: {int((~same).sum())} bf16 outputs differ from the rounded fp32 output"
+    if accum != "exact":
+        return
+    ref = fp8.bf16_bits_to_f64(fp8.bf16_round_bits(y_exact))
+    d = np.abs(fp8.bf16_bits_to_f64(y_bits) - ref)
+    ulp = bf16_ulp(ref)
+    cancel = ulp < 1e-5 * T
+    over = (d > ulp) & ~cancel
+    assert not over.any(), f"{what}: {int(over.sum())} bf16 outputs beyond 1 ulp"
+    assert (d[cancel] <= ulp[cancel] + 1e-5 * T[cancel]).all()
+
+
+def run_case(x, w, *, accum, rows=None, cols=None, w_layout="row_major", a_layout="row_major", what=""):
+    """Quantize X (1 x 128 groups) and W (128 x 128 blocks) on the GPU, check
+    codes and scales against the oracle, run the GEMM, check its outputs."""
+    is_bf16 = x.dtype == np.uint16
+    xt = dev_bf16(x) if is_bf16 else dev(x)
+    xf = f32_from_bf16_bits(x) if is_bf16 else x
+    M, K = xf.shape
+    N = w.shape[0]
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    cols = np.arange(N) if cols is None else np.asarray(cols)
+
+    aq_t, sa_t = sg.fp8_quant_per_token_group(xt)
+    wq_t, sw_t = sg.fp8_quant_weight_blockwise(dev(w))
+    aq_ref, sa_ref = bw.quant_act_blockwise(xf[rows])
+    sw_ref = bw.weight_block_scales(w)
+    aq_got, sa_got, sw_got = host(aq_t)[rows], host(sa_t)[rows], host(sw_t)
+    assert np.array_equal(sa_got.view(np.uint32), sa_ref.view(np.uint32)), f"{what}: activation group scales"
+    assert_codes_equal(aq_got, aq_ref, f"{what}: activation codes")
+    assert np.array_equal(sw_got.view(np.uint32), sw_ref.view(np.uint32)), f"{what}: weight block scales"
+    wq_all = host(wq_t)
+    per_elem = np.repeat(np.repeat(sw_ref, 128, axis=0)[:N], 128, axis=1)[cols]
+    from oracle.w8a8 import f32_div
+    assert_codes_equal(wq_all[cols], fp8.encode(f32_div(w[cols], per_elem)), f"{what}: weight codes")
+
+    a_in = aq_t if a_layout == "row_major" else sg.fp8_pack_weights(aq_t)
+    w_in = wq_t if w_layout == "row_major" else sg.fp8_pack_weights(wq_t)
+    kw = dict(accum=accum, w_layout=w_layout, a_layout=a_layout, a_shape=(M, K), w_shape=(N, K))
+    y32 = sg.fp8_scaled_gemm_blockwise(a_in, sa_t, w_in, sw_t, out_dtype=torch.float32, **kw)
+    y16 = sg.fp8_scaled_gemm_blockwise(a_in, sa_t, w_in, sw_t, **kw)
+    torch.cuda.synchronize()
+    check_gemm(host(y32)[np.ix_(rows, cols)], host_bits16(y16)[np.ix_(rows, cols)], aq_ref, sa_ref, wq_all, sw_ref,
+               cols, accum, what)
+
+
+def _sample(M, N, seed, nr=24, nc=256):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(nr, M), replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(nc, N), replace=False)]))
+    return rows, cols
+
+
+@pytest.mark.parametrize("layout", ["row_major", "packed"])
+@pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
+def test_tiny(accum, layout):
+    x, w = tiny_w8a8(0)
+    run_case(x, w, accum=accum, w_layout=layout, a_layout=layout, what=f"tiny {accum} {layout}")
+
+
+@pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_decode(m, accum):
+    xb, w, _ = decode_inputs(m)
+    _, cols = _sample(m, w.shape[0], m, nc=1024)
+    run_case(xb, w, accum=accum, cols=cols, w_layout="packed", a_layout="packed", what=f"decode M={m} {accum}")
+
+
+@pytest.mark.parametrize("layout", ["row_major", "packed"])
+@pytest.mark.parametrize("m,n,k", [(300, 1000, 1024), (129, 1001, 256), (33, 4100, 512), (17, 515, 128),
+                                   (1, 7, 128), (5, 1, 384), (256, 384, 2048), (520, 130, 384)])
+def test_ragged(m, n, k, layout):
+    rng = np.random.default_rng(m * 7 + n + k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, rng.integers(0, k, 3)] *= 40
+    if k >= 256:
+        x[m // 2, 128:256] = 0.0                                     # an all-zero group (scale 1.0)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    w[: min(n, 128), :128] *= 30                                     # one block with larger weights
+    accums = ["mfma_fp8", "exact"] if m <= 32 else ["mfma_fp8"]
+    for accum in accums:
+        run_case(bf16_bits_from_f32(x), w, accum=accum, w_layout=layout, a_layout=layout,
+                 what=f"ragged {m}x{n}x{k} {accum} {layout}")
+
+
+@pytest.mark.parametrize("k", [4096, 14336])
+def test_prefill_sampled(k):
+    xb, w, _ = prefill_inputs(k)
+    rows, cols = _sample(xb.shape[0], w.shape[0], k)
+    run_case(xb, w, accum="mfma_fp8", rows=rows, cols=cols, w_layout="packed", a_layout="row_major",
+             what=f"prefill K={k}")
+
+
+def test_fp32_input_and_packed_codes():
+    """fp32 activations; the packed quantizer output equals the packed row-major output."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((37, 512)) * np.float32(3.0)).astype(np.float32)
+    x[3, :128] *= 1e-30                                          # a group far down in float32
+    xt = dev(x)
+    q_rm, s_rm = sg.fp8_quant_per_token_group(xt)
+    q_pk = torch.zeros(sg.fp8_packed_weight_bytes(37, 512), dtype=torch.uint8, device="cuda")
+    q_pk, s_pk = sg.fp8_quant_per_token_group(xt, layout="packed", q=q_pk)
+    torch.cuda.synchronize()
+    q_ref, s_ref = bw.quant_act_blockwise(x)
+    assert np.array_equal(host(s_rm).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(s_pk).view(np.uint32), s_ref.view(np.uint32))
+    assert_codes_equal(host(q_rm), q_ref, "fp32 group codes")
+    assert np.array_equal(host(q_pk), pack_reference(q_ref))
+
+
+def test_deterministic_repeats():
+    xb, w, _ = prefill_inputs(1024, m=600, n=700)
+    aq, sa = sg.fp8_quant_per_token_group(dev_bf16(xb))
+    wq, sw = sg.fp8_quant_weight_blockwise(dev(w))
+    outs = [host_bits16(sg.fp8_scaled_gemm_blockwise(aq, sa, wq, sw)) for _ in range(8)]
+    small = [host_bits16(sg.fp8_scaled_gemm_blockwise(aq[:24], sa[:24], wq, sw, accum=a)) for a in ("exact",) * 4]
+    assert all(np.array_equal(o, outs[0]) for o in outs)
+    assert all(np.array_equal(o, small[0]) for o in small)
+
+
+def test_exact_mode_refuses_large_m():
+    aq = torch.zeros((33, 128), dtype=torch.uint8, device="cuda")
+    sa = torch.ones((33, 1), dtype=torch.float32, device="cuda")
+    wq = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
+    sw = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(sg.Fp8sgError) as e:
+        sg.fp8_scaled_gemm_blockwise(aq, sa, wq, sw, accum="exact")
+    assert e.value.status == sg.fp8sg.E_DTYPE
