@@ -65,7 +65,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--quick", action="store_true", help="headline only: skip the detail workloads")
     ap.add_argument("--workload", nargs="*", default=None,
-                    help="detail workloads to run (default all): prefill large quant kv weights")
+                    help="detail workloads to run (default all): prefill large quant kv weights blockwise")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -199,7 +199,7 @@ def main():
                 "timing": "HIP events around 100 back-to-back launches on the library's stream, mean of 5"}
 
     # ------------------------------------------------------------ details
-    wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights"}
+    wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights", "blockwise"}
     if args.quick:
         wanted = set()
     del wqs[1:], wrm[1:]
@@ -379,6 +379,61 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
                     "avg_us": round(float(d.mean()) * 1e3, 1), "GB_s": _gbs(5 * N * K + 4 * N, d.mean()),
                     "frac_hbm": round(_gbs(5 * N * K + 4 * N, d.mean()) / HBM_PEAK_GBS, 4)})
         del w_t
+
+    if "blockwise" in wanted:
+        log("block-wise")
+        from workloads import decode_inputs
+        # decode shape: 1 x 128 activation groups, 128 x 128 weight blocks, packed operands
+        _, w, _ = decode_inputs(1)
+        w_t = torch.from_numpy(w).to(dev)
+        N, K = w.shape
+        d = timed_events(lambda i: sg.fp8_quant_weight_blockwise(w_t), 20, 3, reps=3)
+        out.append({"workload": f"block-wise weight quant W fp32 [{N},{K}] 128x128 blocks (offline)",
+                    "avg_us": round(float(d.mean()) * 1e3, 1), "GB_s": _gbs(5 * N * K, d.mean())})
+        wq, sw = sg.fp8_quant_weight_blockwise(w_t)
+        wp = sg.fp8_pack_weights(wq)
+        wps = copies(wp, 8)
+        del w_t, wq
+        for m in (1, 8, 32):
+            xb, _, _ = decode_inputs(m, with_weight=False)
+            x = to_bf16(xb)
+            aq, sa = sg.fp8_quant_per_token_group(x, layout="packed")
+            y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            d = timed_events(lambda i: sg.fp8_quant_per_token_group(x, layout="packed", q=aq, scales=sa), 100, 20)
+            out.append({"workload": f"block-wise act quant 1x128 X bf16 [{m},{K}]",
+                        "avg_us": round(float(d.mean()) * 1e3, 2)})
+            for accum in ("exact", "mfma_fp8"):
+                d = timed_events(lambda i: sg.fp8_scaled_gemm_blockwise(aq, sa, wps[i % 8], sw, y=y, accum=accum,
+                                                                        w_layout="packed", a_layout="packed",
+                                                                        a_shape=(m, K), w_shape=(N, K)), 100, 20)
+                kb = N * K + 4 * sw.numel() + m * K + 4 * sa.numel() + 2 * m * N
+                out.append({"workload": f"block-wise decode GEMM M={m} N={N} K={K}", "accum": accum,
+                            "avg_us": round(float(d.mean()) * 1e3, 2), "GB_s": _gbs(kb, d.mean()),
+                            "frac_hbm": round(_gbs(kb, d.mean()) / HBM_PEAK_GBS, 4)})
+        del wps, wp
+        torch.cuda.empty_cache()
+        # prefill shapes
+        for K in (4096, 14336):
+            xb, w, _ = prefill_inputs(K)
+            M, N = xb.shape[0], w.shape[0]
+            xl = copies(to_bf16(xb), 2)
+            aq, sa = sg.fp8_quant_per_token_group(xl[0])
+            d = timed_events(lambda i: sg.fp8_quant_per_token_group(xl[i % 2], q=aq, scales=sa), 20, 3, reps=3)
+            gbs = _gbs(3 * M * K + 4 * M * (K // 128), d.mean())
+            out.append({"workload": f"block-wise act quant 1x128 X bf16 [{M},{K}]",
+                        "avg_us": round(float(d.mean()) * 1e3, 2), "GB_s": gbs,
+                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+            wq, sw = sg.fp8_quant_weight_blockwise(torch.from_numpy(w).to(dev))
+            wp = sg.fp8_pack_weights(wq)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            d = timed_events(lambda i: sg.fp8_scaled_gemm_blockwise(aq, sa, wp, sw, y=y, accum="mfma_fp8",
+                                                                    w_layout="packed", w_shape=(N, K)), 10, 3, reps=3)
+            tf = _tflops(2.0 * M * N * K, d.mean())
+            out.append({"workload": f"block-wise prefill GEMM {M}x{N}x{K}", "accum": "mfma_fp8",
+                        "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
+                        "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
+            del xl, aq, sa, wq, wp, y
+            torch.cuda.empty_cache()
 
     if "kv" in wanted:
         log("kv cache")

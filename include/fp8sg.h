@@ -159,10 +159,12 @@ size_t fp8_packed_weight_bytes(int64_t N, int64_t K);
 fp8sg_status fp8_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, void* stream);
 
 /*
- * Bytes of device workspace fp8_scaled_gemm needs for these arguments (0 when
- * the activation arrives already quantized): the codes it quantizes, in the
- * fragment order with rows padded to a multiple of 16 when M <= 32, row-major
- * otherwise, then (per-token mode without a caller buffer) the scales.
+ * Bytes of device workspace fp8_scaled_gemm needs for these arguments: the
+ * codes it quantizes, in the fragment order with rows padded to a multiple of
+ * 16 when M <= 32, row-major otherwise, then (per-token mode without a caller
+ * buffer) the scales.  0 when the activation arrives already quantized, and
+ * for bf16 per-token activations with M <= 4 and K <= 4096, which the decode
+ * kernel quantizes itself (in LDS, while its weight loads are in flight).
  * Host-only; no HIP call.
  */
 size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, int64_t N, int64_t K);

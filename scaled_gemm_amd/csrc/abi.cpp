@@ -132,6 +132,8 @@ size_t quantized_a_bytes(int64_t M, int64_t K) {
 size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, int64_t N, int64_t K) {
     (void)N;
     if (!is_hp(a_dtype) || M <= 0 || K < 0) return 0;
+    // decode-sized per-token activations are quantized inside the GEMM kernel itself
+    if (a_scale_mode == FP8SG_SCALE_PER_TOKEN && fp8sg::gemm_fused_quant_fits(a_dtype == FP8SG_BF16, M, K)) return 0;
     size_t bytes = quantized_a_bytes(M, K);
     if (a_scale_mode == FP8SG_SCALE_PER_TOKEN) bytes += align256((size_t)M * 4);
     return bytes;
@@ -183,6 +185,12 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
     if (d != FP8SG_OK) return d;
     hipStream_t s = (hipStream_t)stream;
 
+    if (quantize_here && per_token && fp8sg::gemm_fused_quant_fits(a_dtype == FP8SG_BF16, M, K)) {
+        return launched(fp8sg::launch_gemm_fused_quant((const uint16_t*)a, a_scales, wq,
+                                                       (layout & FP8SG_W_PACKED) != 0, w_scales, y,
+                                                       y_dtype == FP8SG_BF16, M, N, K,
+                                                       accum == FP8SG_ACCUM_MFMA_FP8, s));
+    }
     const uint8_t* aq = (const uint8_t*)a;
     const float* sa = a_scales;
     if (quantize_here) {

@@ -154,4 +154,36 @@ __device__ __forceinline__ float dynamic_scale(float amax, float fmax) {
     return s == 0.0f ? 1.0f : s;
 }
 
+// A chunk is 8 consecutive elements: one 16-byte load for bf16, two for fp32.
+template <typename InT>
+__device__ __forceinline__ void load_chunk(const InT* p, float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load_chunk<uint16_t>(const uint16_t* p, float (&v)[8]) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+    v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+    v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+}
+
+template <>
+__device__ __forceinline__ void load_chunk<float>(const float* p, float (&v)[8]) {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename InT>
+__device__ __forceinline__ uint2 encode_chunk_dynamic(const float (&v)[8], const QScale& p) {
+    constexpr bool kTwo = sizeof(InT) == 4;
+    uint2 o;
+    o.x = pack4<0>(quotient_dynamic<kTwo>(v[0], p), quotient_dynamic<kTwo>(v[1], p),
+                   quotient_dynamic<kTwo>(v[2], p), quotient_dynamic<kTwo>(v[3], p));
+    o.y = pack4<0>(quotient_dynamic<kTwo>(v[4], p), quotient_dynamic<kTwo>(v[5], p),
+                   quotient_dynamic<kTwo>(v[6], p), quotient_dynamic<kTwo>(v[7], p));
+    return o;
+}
+
 }  // namespace fp8sg

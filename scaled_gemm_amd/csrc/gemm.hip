@@ -1031,6 +1031,214 @@ hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* 
 }
 
 // ---------------------------------------------------------------------------
+// Decode GEMM with the per-token activation quantization fused in (bf16 X,
+// M <= 4, K <= 4096): X [M, K] in, Y out, one launch.
+//
+// The dynamic per-token rule needs each row's maximum before any code, and
+// every workgroup needs all of A, so each workgroup quantizes the few rows
+// itself, while the weight stream is already under way: a wave first issues
+// the loads of its X chunks (one chunk of 8 per thread and row), then the
+// loads of ALL its W blocks (at most kFusedMaxPer, held in registers), and only
+// then waits for X.  Loads complete in issue order, so X arrives first and the
+// quantization (row maxima by wave shuffles and LDS, encode, codes to LDS with
+// rows K + 16 bytes apart) runs while W is in flight.  Rows, chunks and blocks
+// past the valid ones are clamped to valid addresses and masked, so the code
+// between the loads has no branches.  8 waves of at most 128 registers each:
+// the whole weight matrix of the decode shape is then requested at once by
+// workgroups that all fit on the chip together (two per CU).  Workgroup 0
+// also writes the scales for the caller.  The multiplies are the skinny
+// kernel's: W fragments from registers, A fragments from LDS, k blocks split
+// round-robin over the waves, partial sums added in fixed order.
+constexpr int kFusedMaxM = 4;      // rows: with more, the X registers push the wave past 128 VGPRs
+constexpr int kFusedKS = 8;         // waves per workgroup
+constexpr int kFusedRowChunks = 1;  // chunks of 8 per thread and row: K <= 8 * 1 * 64 * kFusedKS
+constexpr int kFusedMaxPer = 4;     // W blocks per wave: K <= 128 * 4 * kFusedKS
+
+__device__ __forceinline__ Frag load_frag_lds(const uint8_t* p) {
+    Frag f;
+    f.lo = reinterpret_cast<const uint4*>(p)[0];
+    f.hi = reinterpret_cast<const uint4*>(p)[1];
+    return f;
+}
+
+template <bool kFp8, bool kYbf16, bool kWPacked, int kNS, int kKS, int kM>
+__global__ __launch_bounds__(64 * kKS) __attribute__((amdgpu_waves_per_eu(4))) void gemm_skinny_fused(
+    const uint16_t* __restrict__ X, float* __restrict__ sa_out, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];  // [M][K + 16] codes
+    __shared__ f32x4 red[kKS > 1 ? kKS - 1 : 1][kNS][64];
+    __shared__ float row_max[kKS][kFusedMaxM];
+    __shared__ float row_scale[kFusedMaxM];
+    constexpr int T = 64 * kKS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * kNS);
+    const int nkb = K >> 7;
+    const int r16 = lane & 15, kofs = (lane >> 4) * 32;
+    const int pitch = K + 16;
+    const int row_chunks = K >> 3;
+
+    // 1. X: this thread's chunks of every row (clamped to valid rows / chunks)
+    uint4 xr[kM][kFusedRowChunks];
+#pragma unroll
+    for (int r = 0; r < kM; ++r) {
+        const int rr = r < M ? r : M - 1;
+#pragma unroll
+        for (int i = 0; i < kFusedRowChunks; ++i) {
+            int c = threadIdx.x + i * T;
+            c = c < row_chunks ? c : row_chunks - 1;
+            xr[r][i] = *reinterpret_cast<const uint4*>(X + (int64_t)rr * K + (int64_t)c * 8);
+        }
+    }
+
+    // 2. W: every block of this wave (wave + j * kKS, j < nper; clamped past the end)
+    const int nper = nkb > wave ? (nkb - wave + kKS - 1) / kKS : 0;
+    const uint8_t* wrow[kNS];
+    const int64_t last_tile = ((int64_t)N + 15) / 16 - 1;
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+        if (kWPacked) {
+            int64_t t = (n_base >> 4) + s;
+            t = t < last_tile ? t : last_tile;
+            wrow[s] = W + t * nkb * kPackBlock;
+        } else {
+            int64_t n = n_base + 16 * s + r16;
+            n = n < N ? n : N - 1;
+            wrow[s] = W + n * (int64_t)K + kofs;
+        }
+    }
+    Frag wf[kFusedMaxPer][kNS];
+#pragma unroll
+    for (int j = 0; j < kFusedMaxPer; ++j) {
+        int jj = j < nper ? j : nper - 1;
+        jj = jj > 0 ? jj : 0;
+        int kb = wave + jj * kKS;
+        kb = kb < nkb ? kb : nkb - 1;  // a wave without blocks (nper == 0) loads block nkb - 1, unused
+#pragma unroll
+        for (int s = 0; s < kNS; ++s)
+            wf[j][s] = kWPacked ? load_frag_packed(wrow[s] + kb * kPackBlock, lane)
+                                : load_frag_global(wrow[s] + ((int64_t)kb << 7));
+    }
+
+    // 3. row maxima and scales
+#pragma unroll
+    for (int r = 0; r < kM; ++r) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kFusedRowChunks; ++i) {
+            const uint4 u = xr[r][i];
+            const float a = fmaxf(fmaxf(fmaxf(__builtin_fabsf(bf16_lo(u.x)), __builtin_fabsf(bf16_hi(u.x))),
+                                        fmaxf(__builtin_fabsf(bf16_lo(u.y)), __builtin_fabsf(bf16_hi(u.y)))),
+                                  fmaxf(fmaxf(__builtin_fabsf(bf16_lo(u.z)), __builtin_fabsf(bf16_hi(u.z))),
+                                        fmaxf(__builtin_fabsf(bf16_lo(u.w)), __builtin_fabsf(bf16_hi(u.w)))));
+            const bool valid = (int)threadIdx.x + i * T < row_chunks;
+            amax = valid ? fmaxf(amax, a) : amax;
+        }
+        amax = wave_max(amax);
+        if (lane == 0) row_max[wave][r] = amax;
+    }
+    __syncthreads();
+    if (threadIdx.x < kM) {
+        float m = row_max[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < kKS; ++w) m = fmaxf(m, row_max[w][threadIdx.x]);
+        const float sc = dynamic_scale(m, kE4M3Max);
+        row_scale[threadIdx.x] = sc;
+        if (blockIdx.x == 0 && sa_out != nullptr && (int)threadIdx.x < M) sa_out[threadIdx.x] = sc;
+    }
+    __syncthreads();
+
+    // 4. codes to LDS
+#pragma unroll
+    for (int r = 0; r < kM; ++r) {
+        if (r < M) {
+            const QScale p = make_qscale(row_scale[r], kE4M3Max);
+#pragma unroll
+            for (int i = 0; i < kFusedRowChunks; ++i) {
+                const int c = threadIdx.x + i * T;
+                if (c < row_chunks) {
+                    float v[8];
+                    const uint4 u = xr[r][i];
+                    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+                    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+                    *reinterpret_cast<uint2*>(a_lds + r * pitch + c * 8) = encode_chunk_dynamic<uint16_t>(v, p);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // 5. the multiplies of this wave's blocks
+    f32x4 acc[kNS];
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t* arow = a_lds + (r16 < M ? r16 : M - 1) * pitch + kofs;
+#pragma unroll
+    for (int j = 0; j < kFusedMaxPer; ++j) {
+        if (j < nper) {
+            const Frag af = load_frag_lds(arow + (wave + j * kKS) * 128);
+#pragma unroll
+            for (int s = 0; s < kNS; ++s) acc[s] = mma<kFp8>(wf[j][s], af, acc[s]);
+        }
+    }
+
+    if (kKS > 1) {
+        if (wave > 0) {
+#pragma unroll
+            for (int s = 0; s < kNS; ++s) red[wave - 1][s][lane] = acc[s];
+        }
+        __syncthreads();
+    }
+    if (wave == 0) {
+        const bool vec_ok = (N & 3) == 0;
+        const int m = r16;
+#pragma unroll
+        for (int s = 0; s < kNS; ++s) {
+            f32x4 a = acc[s];
+#pragma unroll
+            for (int w = 0; w < kKS - 1; ++w) a += red[w][s][lane];
+            const int64_t n0 = n_base + 16 * s + 4 * (lane >> 4);
+            if (m < M && n0 < N) store4<kYbf16>(Y, N, m, n0, a, row_scale[m], sw, vec_ok);
+        }
+    }
+}
+
+template <bool kFp8, bool kYbf16, bool kWPacked>
+static void launch_fused_t(const uint16_t* x, float* sa_out, const uint8_t* wq, const float* sw, void* y, int M,
+                           int N, int K, hipStream_t stream) {
+    dim3 grid((unsigned)((N + 16 * SKINNY_NS - 1) / (16 * SKINNY_NS))), block(64 * kFusedKS);
+    const size_t lds = (size_t)M * (size_t)(K + 16);
+#define FP8SG_FUSED_M(KM) \
+    gemm_skinny_fused<kFp8, kYbf16, kWPacked, SKINNY_NS, kFusedKS, KM><<<grid, block, lds, stream>>>(x, sa_out, wq, sw, \
+                                                                                                  y, M, N, K)
+    if (M <= 1) FP8SG_FUSED_M(1);
+    else if (M <= 2) FP8SG_FUSED_M(2);
+    else FP8SG_FUSED_M(4);
+#undef FP8SG_FUSED_M
+}
+
+bool gemm_fused_quant_fits(bool x_is_bf16, int64_t M, int64_t K) {
+    return x_is_bf16 && M >= 1 && M <= kFusedMaxM && K <= (int64_t)8 * kFusedRowChunks * 64 * kFusedKS &&
+           K <= (int64_t)128 * kFusedMaxPer * kFusedKS;
+}
+
+hipError_t launch_gemm_fused_quant(const uint16_t* x, float* sa_out, const uint8_t* wq, bool w_packed,
+                                   const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
+                                   bool fp8_mfma, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    const int m = (int)M, n = (int)N, k = (int)K;
+#define FP8SG_FUSED(F8, YB, WP) launch_fused_t<F8, YB, WP>(x, sa_out, wq, w_scales, y, m, n, k, stream)
+    if (fp8_mfma) {
+        if (y_bf16) w_packed ? FP8SG_FUSED(true, true, true) : FP8SG_FUSED(true, true, false);
+        else w_packed ? FP8SG_FUSED(true, false, true) : FP8SG_FUSED(true, false, false);
+    } else {
+        if (y_bf16) w_packed ? FP8SG_FUSED(false, true, true) : FP8SG_FUSED(false, true, false);
+        else w_packed ? FP8SG_FUSED(false, false, true) : FP8SG_FUSED(false, false, false);
+    }
+#undef FP8SG_FUSED
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Weight packing: one thread per 16-byte chunk of the packed buffer.  Chunk c
 // belongs to block c / 128 = (tile t, k block kb) and to half h = (c % 128) / 64
 // of lane l = c % 64, which reads row 16 t + l % 16 at byte kb * 128 + 32 (l / 16)

@@ -30,6 +30,13 @@ hipError_t launch_gemm(const uint8_t* aq, bool a_packed, const float* a_scales, 
                        bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
                        bool fp8_mfma, hipStream_t stream);
 
+// Decode GEMM with the per-token activation quantization inside the same
+// kernel (bf16 X), for the shapes gemm_fused_quant_fits accepts.  sa_out may be NULL.
+bool gemm_fused_quant_fits(bool x_is_bf16, int64_t M, int64_t K);
+hipError_t launch_gemm_fused_quant(const uint16_t* x, float* sa_out, const uint8_t* wq, bool w_packed,
+                                   const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
+                                   bool fp8_mfma, hipStream_t stream);
+
 // Block-wise scaled GEMM: a_scales [M, K/128], w_scales [ceil(N/128), K/128].
 hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* a_scales, const uint8_t* wq,
                                  bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N,

@@ -115,17 +115,23 @@ def test_gemm_validation(lib):
     assert call(M=0) == b.OK
     # a bf16 activation needs the workspace the size query reports: the codes
     # (fragment order, rows padded to 16, for M <= 32; row-major above), then
-    # the per-token scales
-    need = lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4, 8, 128)
+    # the per-token scales -- except bf16 per-token with M <= 4 and K <= 4096,
+    # which the decode kernel quantizes itself (no workspace)
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4, 8, 128) == 0
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 1, 8, 4096) == 0
+    assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TOKEN, 1, 8, 4096) == 16 * 4096 + 256
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4, 8, 4224) == 16 * 4224 + 256
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 5, 8, 128) == 16 * 128 + 256
+    need = lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 12, 8, 128)
     assert need == 16 * 128 + 256
     assert lib.fp8_scaled_gemm_workspace_size(b.E4M3, b.SCALE_PER_TOKEN, 4, 8, 128) == 0
     assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TENSOR, 4, 8, 128) == 16 * 128
     assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TENSOR, 17, 8, 256) == 32 * 256
     assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TENSOR, 33, 8, 256) == 33 * 256
     assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 33, 8, 128) == 4352 + 256  # 33 * 128 rounded up to 256
-    assert call(a_dt=b.BF16, sa=None) == b.E_WORKSPACE
-    assert call(a_dt=b.BF16, sa=None, ws=A, wsb=need - 1) == b.E_WORKSPACE
-    assert call(a_dt=b.BF16, sa=None, ws=A + 16, wsb=need) == b.E_ALIGN
+    assert call(a_dt=b.BF16, sa=None, M=12) == b.E_WORKSPACE
+    assert call(a_dt=b.BF16, sa=None, M=12, ws=A, wsb=need - 1) == b.E_WORKSPACE
+    assert call(a_dt=b.BF16, sa=None, M=12, ws=A + 16, wsb=need) == b.E_ALIGN
     assert call(a_dt=b.BF16, mode=b.SCALE_PER_TENSOR, sa=None, ws=A, wsb=need) == b.E_NULL
 
 

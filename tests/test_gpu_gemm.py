@@ -52,8 +52,14 @@ def fp8_mfma_bound(aq_rows: np.ndarray, wq_rows: np.ndarray) -> np.ndarray:
     return out
 
 
-def check_outputs(y_bits, acc_gpu, aq_rows, sa_rows, wq_rows, sw_rows, accum, what):
-    """y_bits: bf16 output [r, c]; acc_gpu: fp32 accumulator [r, c] (unit scales)."""
+def check_outputs(y_bits, acc_gpu, aq_rows, sa_rows, wq_rows, sw_rows, accum, what, y_f32_fused=None):
+    """y_bits: bf16 output [r, c]; acc_gpu: fp32 accumulator [r, c] (unit scales).
+
+    y_f32_fused: when y_bits came from the decode kernel that quantizes the
+    activations itself (its k order differs from the unit-scale call's), that
+    kernel's fp32 output; its bf16 rounding must equal y_bits bit for bit, and
+    it must lie within the accumulator bound (scaled) plus the epilogue's two
+    float32 roundings of the exact result."""
     acc = w8a8.gemm_acc_exact(aq_rows, wq_rows)
     absum = w8a8.gemm_abs_sum(aq_rows, wq_rows)
     err = np.abs(acc_gpu.astype(np.float64) - acc)
@@ -64,11 +70,19 @@ def check_outputs(y_bits, acc_gpu, aq_rows, sa_rows, wq_rows, sw_rows, accum, wh
     bad = err > bound
     assert not bad.any(), (f"{what}: accumulator outside tolerance at {int(bad.sum())} outputs; "
                            f"worst err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}")
-    # the bf16 epilogue of the same accumulator: y = bf16_rne(RN32(RN32(acc * s_a) * s_w)), bit for bit
-    # (the fp32 output with unit scales shares the bf16 kernel's main loop, so acc_gpu is its accumulator)
     sa32 = np.asarray(sa_rows, np.float32).reshape(-1, 1)
     sw32 = np.asarray(sw_rows, np.float32).reshape(1, -1)
-    y_epi = fp8.bf16_round_bits(((acc_gpu.astype(np.float32) * sa32) * sw32).astype(np.float64))
+    if y_f32_fused is None:
+        # the bf16 epilogue of the same accumulator: y = bf16_rne(RN32(RN32(acc * s_a) * s_w)), bit for bit
+        # (the fp32 output with unit scales shares the bf16 kernel's main loop, so acc_gpu is its accumulator)
+        y_epi = fp8.bf16_round_bits(((acc_gpu.astype(np.float32) * sa32) * sw32).astype(np.float64))
+    else:
+        y_epi = fp8.bf16_round_bits(y_f32_fused.astype(np.float64))
+        s_abs = np.abs(sa32.astype(np.float64) * sw32.astype(np.float64))
+        y_ex = w8a8.scaled_gemm_f64(acc, sa_rows, sw_rows)
+        e_y = np.abs(y_f32_fused.astype(np.float64) - y_ex)
+        b_y = bound * s_abs * (1 + 2.0 ** -22) + 2.0 ** -22 * np.abs(y_ex)
+        assert (e_y <= b_y).all(), f"{what}: fused fp32 output outside the scaled bound at {int((e_y > b_y).sum())}"
     mism = y_epi != y_bits
     assert not mism.any(), f"{what}: {int(mism.sum())} bf16 outputs differ from the scaled accumulator"
     if accum != "exact":
@@ -108,9 +122,14 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
     assert np.array_equal(sw_got.view(np.uint32), sw_ref.view(np.uint32)), f"{what}: weight scales"
     assert_codes_equal(wq_got, wq_ref, f"{what}: weight codes")
 
+    y32_fused = None
     if static is None:
         sa_t = torch.empty(M, dtype=torch.float32, device="cuda")
         y_t = sg.fp8_scaled_gemm(xt, sa_t, wg, sw_t, a_scale_mode="per_token", accum=accum, w_layout=layout)
+        if is_bf16 and sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", M, N, K) == 0:
+            # quantized inside the decode kernel: the same kernel's fp32 output checks its epilogue
+            y32_fused = sg.fp8_scaled_gemm(xt, None, wg, sw_t, out_dtype=torch.float32, accum=accum,
+                                           w_layout=layout)
         aq_ref, sa_ref = w8a8.quant_per_token(xf[rows])
         assert np.array_equal(host(sa_t)[rows].view(np.uint32), sa_ref.view(np.uint32)), f"{what}: act scales"
         # the accumulator through the same kernel: pre-quantized codes, unit scales, fp32 out
@@ -138,7 +157,8 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
     acc_pk = host(acc_p)[np.ix_(rows, cols)]
     assert np.array_equal(acc_pk.view(np.uint32), acc_gpu.view(np.uint32)), f"{what}: packed-A accumulator differs"
     del ap_t, acc_p
-    check_outputs(y_bits, acc_gpu, aq_ref, sa_ref, wq_ref, sw_ref, accum, what)
+    y32f = None if y32_fused is None else host(y32_fused)[np.ix_(rows, cols)]
+    check_outputs(y_bits, acc_gpu, aq_ref, sa_ref, wq_ref, sw_ref, accum, what, y_f32_fused=y32f)
 
 
 ACCUMS = ["exact", "mfma_fp8"]
@@ -257,11 +277,14 @@ def test_fp8_matrix_core_group_alignment_is_what_exact_mode_avoids():
 
 
 def test_workspace_and_errors():
-    x = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
+    # decode-sized (M <= 4) per-token activations are quantized inside the GEMM kernel: no workspace
+    assert sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", 4, 8, 128) == 0
+    assert sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_tensor", 4, 8, 128) >= 4 * 128
+    x = torch.zeros((40, 128), dtype=torch.bfloat16, device="cuda")
     wq = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
     sw = torch.ones(8, dtype=torch.float32, device="cuda")
-    need = sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", 4, 8, 128)
-    assert need >= 4 * 128
+    need = sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", 40, 8, 128)
+    assert need >= 40 * 128
     small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
     with pytest.raises(sg.Fp8sgError) as e:
         sg.fp8_scaled_gemm(x, None, wq, sw, workspace=small)
@@ -269,3 +292,35 @@ def test_workspace_and_errors():
     y = sg.fp8_scaled_gemm(x, None, wq, sw)
     torch.cuda.synchronize()
     assert (host_bits16(y) == 0).all()
+
+@pytest.mark.parametrize("accum", ACCUMS)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_fused_decode_quant(accum, layout):
+    """For bf16 activations with M <= 4 and K <= 4096 the per-token quantization
+    runs inside the GEMM kernel.  Its scales must equal fp8_quant_per_token's
+    bit for bit; its output must not depend on whether the scales are returned;
+    and its output must meet the oracle checks (the 1-ulp / accumulator bounds),
+    also at K = 4224 (past the limit: the two-kernel path) and for fp32
+    activations (always the two-kernel path)."""
+    rng = np.random.default_rng(5)
+    from workloads import bf16_bits_from_f32
+    for m, n, k in ((1, 300, 4096), (3, 1000, 128), (4, 4100, 4096), (4, 77, 4224), (2, 33, 1152), (5, 64, 256)):
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        x[:, rng.integers(0, k, 3)] *= 40
+        xb = bf16_bits_from_f32(x)
+        w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        what = f"fused {m}x{n}x{k} {accum} {layout}"
+        gemm_case(xb, w, accum=accum, what=what, layout=layout)
+        wq, sw = sg.fp8_quant_weight_per_channel(dev(w))
+        wg = sg.fp8_pack_weights(wq) if layout == "packed" else wq
+        xt = dev_bf16(xb)
+        sa = torch.empty(m, dtype=torch.float32, device="cuda")
+        y1 = sg.fp8_scaled_gemm(xt, sa, wg, sw, accum=accum, w_layout=layout)
+        y0 = sg.fp8_scaled_gemm(xt, None, wg, sw, accum=accum, w_layout=layout)
+        _, sa2 = sg.fp8_quant_per_token(xt)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(sa).view(np.uint32), host(sa2).view(np.uint32)), what
+        assert np.array_equal(host_bits16(y1), host_bits16(y0)), what
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    w = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    gemm_case(x, w, accum=accum, what=f"fp32 activations {accum} {layout}", layout=layout)
