@@ -202,6 +202,26 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Scaled GEMM with an FP8 output epilogue: the result is written as the E4M3
+ * input of a next layer that takes a static per-tensor activation scale, so no
+ * separate quantization pass reads Y again (FP8 Inference Explained, in depth
+ * -- "Scales and their granularity": engines fold the activation quantization
+ * into the kernel that produces the activation; Quantization: FP8 inference and
+ * KV-cache quantization -- "Dynamic scales or static scales": a static scale
+ * costs nothing at run time, values beyond it saturate).
+ *   All arguments as for fp8_scaled_gemm, except:
+ *   out_scale  [1] fp32 (device), the per-tensor scale of the output codes,
+ *              positive and finite
+ *   y          [M, N] E4M3 codes (output): y_code = E4M3(RN32(y32 / out_scale)),
+ *              saturating, where y32 is exactly the fp32 value fp8_scaled_gemm
+ *              writes with y_dtype FP8SG_F32 for the same arguments.
+ */
+fp8sg_status fp8_scaled_gemm_fp8out(const void* a, int a_dtype, float* a_scales, int a_scale_mode,
+                                    const uint8_t* wq, int layout, const float* w_scales,
+                                    const float* out_scale, uint8_t* y, int64_t M, int64_t N, int64_t K,
+                                    int accum, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Block-wise dynamic activation quantization: one scale per token and group of
  * 128 consecutive k, so an outlier widens the step of its own group only (FP8
  * Quantization notebook -- "Granularity"; FP8 Inference Explained, in depth --

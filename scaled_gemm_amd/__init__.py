@@ -32,6 +32,7 @@ from .fp8sg import (  # noqa: F401
     fp8_quant_weight_per_channel,
     fp8_scaled_gemm,
     fp8_scaled_gemm_blockwise,
+    fp8_scaled_gemm_fp8out,
     fp8_scaled_gemm_workspace_size,
     lib,
     status_string,

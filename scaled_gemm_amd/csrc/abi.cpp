@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -154,11 +154,13 @@ fp8sg_status fp8_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* 
     return launched(fp8sg::launch_pack_weights(wq, N, K, wp, (hipStream_t)stream));
 }
 
-fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
-                             int layout, const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
-                             int accum, void* workspace, size_t workspace_bytes, void* stream) {
+static // fp8_scaled_gemm and fp8_scaled_gemm_fp8out: out_kind fp8sg::kOutF32 / kOutBF16 /
+// kOutE4M3 (then out_scale [1] is the per-tensor output scale).
+fp8sg_status scaled_gemm_impl(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
+                              int layout, const float* w_scales, void* y, int out_kind, const float* out_scale,
+                              int64_t M, int64_t N, int64_t K, int accum, void* workspace, size_t workspace_bytes,
+                              void* stream) {
     if (!(a_dtype == FP8SG_E4M3 || is_hp(a_dtype))) return FP8SG_E_DTYPE;
-    if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
     if (!(a_scale_mode == FP8SG_SCALE_PER_TOKEN || a_scale_mode == FP8SG_SCALE_PER_TENSOR)) return FP8SG_E_DTYPE;
     if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
     if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED)) != 0) return FP8SG_E_DTYPE;
@@ -167,6 +169,7 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
     if (K % 128 != 0) return FP8SG_E_SHAPE;
     if (M == 0 || N == 0) return FP8SG_OK;
     if (!y || !w_scales) return FP8SG_E_NULL;
+    if (out_kind == fp8sg::kOutE4M3 && !out_scale) return FP8SG_E_NULL;
     if (K > 0 && (!a || !wq)) return FP8SG_E_NULL;
     const bool per_token = a_scale_mode == FP8SG_SCALE_PER_TOKEN;
     const bool quantize_here = is_hp(a_dtype);
@@ -176,6 +179,7 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
     }
     if ((a && !aligned(a, 16)) || (wq && !aligned(wq, 16)) || !aligned(y, 16)) return FP8SG_E_ALIGN;
     if ((a_scales && !aligned(a_scales, 4)) || !aligned(w_scales, 4)) return FP8SG_E_ALIGN;
+    if (out_scale && !aligned(out_scale, 4)) return FP8SG_E_ALIGN;
     const size_t need = fp8_scaled_gemm_workspace_size(a_dtype, a_scale_mode, M, N, K);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return FP8SG_E_WORKSPACE;
@@ -187,9 +191,8 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
 
     if (quantize_here && per_token && fp8sg::gemm_fused_quant_fits(a_dtype == FP8SG_BF16, M, K)) {
         return launched(fp8sg::launch_gemm_fused_quant((const uint16_t*)a, a_scales, wq,
-                                                       (layout & FP8SG_W_PACKED) != 0, w_scales, y,
-                                                       y_dtype == FP8SG_BF16, M, N, K,
-                                                       accum == FP8SG_ACCUM_MFMA_FP8, s));
+                                                       (layout & FP8SG_W_PACKED) != 0, w_scales, y, out_kind,
+                                                       out_scale, M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, s));
     }
     const uint8_t* aq = (const uint8_t*)a;
     const float* sa = a_scales;
@@ -210,7 +213,25 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
     }
     const bool a_packed = quantize_here ? pack_here : (layout & FP8SG_A_PACKED) != 0;
     return launched(fp8sg::launch_gemm(aq, a_packed, sa, per_token, wq, (layout & FP8SG_W_PACKED) != 0, w_scales, y,
-                                       y_dtype == FP8SG_BF16, M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, s));
+                                       out_kind, out_scale, M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, s));
+}
+
+
+fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
+                             int layout, const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                             int accum, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
+    return scaled_gemm_impl(a, a_dtype, a_scales, a_scale_mode, wq, layout, w_scales, y,
+                            y_dtype == FP8SG_BF16 ? fp8sg::kOutBF16 : fp8sg::kOutF32, nullptr, M, N, K, accum,
+                            workspace, workspace_bytes, stream);
+}
+
+fp8sg_status fp8_scaled_gemm_fp8out(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
+                                    int layout, const float* w_scales, const float* out_scale, uint8_t* y, int64_t M,
+                                    int64_t N, int64_t K, int accum, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    return scaled_gemm_impl(a, a_dtype, a_scales, a_scale_mode, wq, layout, w_scales, y, fp8sg::kOutE4M3, out_scale, M,
+                            N, K, accum, workspace, workspace_bytes, stream);
 }
 
 fp8sg_status fp8_quant_per_token_group(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* q, float* scales,

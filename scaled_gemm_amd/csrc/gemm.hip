@@ -93,32 +93,48 @@ __device__ __forceinline__ Frag load_frag_packed(const uint8_t* block, int lane)
     return f;
 }
 
+// Output kinds (kOutF32 / kOutBF16 / kOutE4M3, launch.h): for E4M3 the code of
+// the fp32 result y is FMT(RN32(y / s_out)) with the given per-tensor output
+// scale s_out, saturating -- the input of a next layer that takes static
+// per-tensor activation scales.
+template <int kOut>
+__device__ __forceinline__ QScale out_qscale(const float* __restrict__ qs) {
+    return make_qscale(kOut == kOutE4M3 ? qs[0] : 1.0f, kE4M3Max);
+}
+
+// Four fp32 results -> four E4M3 codes (byte r = code of v[r]).
+__device__ __forceinline__ uint32_t out_codes4(float v0, float v1, float v2, float v3, const QScale& q) {
+    return pack4<0>(quotient_given<true>(v0, q), quotient_given<true>(v1, q), quotient_given<true>(v2, q),
+                    quotient_given<true>(v3, q));
+}
+
 // Epilogue for one 16x16 fragment: lane holds acc[r] = C[n0 + r][m], r = 0..3.
 // store4 applies the per-token / per-channel scales; store4_raw stores the
 // values as they are (block-wise scales were applied inside the k loop).
-template <bool kYbf16>
+template <int kOut>
 __device__ __forceinline__ void store4_vals(void* y, int64_t N, int64_t m, int64_t n0, const float (&v)[4],
-                                           bool vec_ok);
+                                           bool vec_ok, const QScale& q);
 
-template <bool kYbf16>
-__device__ __forceinline__ void store4_raw(void* y, int64_t N, int64_t m, int64_t n0, f32x4 acc, bool vec_ok) {
+template <int kOut>
+__device__ __forceinline__ void store4_raw(void* y, int64_t N, int64_t m, int64_t n0, f32x4 acc, bool vec_ok,
+                                           const QScale& q) {
     const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    store4_vals<kYbf16>(y, N, m, n0, v, vec_ok);
+    store4_vals<kOut>(y, N, m, n0, v, vec_ok, q);
 }
 
-template <bool kYbf16>
+template <int kOut>
 __device__ __forceinline__ void store4(void* y, int64_t N, int64_t m, int64_t n0, f32x4 acc, float sa,
-                                       const float* __restrict__ sw, bool vec_ok) {
+                                       const float* __restrict__ sw, bool vec_ok, const QScale& q) {
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = (n0 + r < N) ? (acc[r] * sa) * sw[n0 + r] : 0.0f;
-    store4_vals<kYbf16>(y, N, m, n0, v, vec_ok);
+    store4_vals<kOut>(y, N, m, n0, v, vec_ok, q);
 }
 
-template <bool kYbf16>
+template <int kOut>
 __device__ __forceinline__ void store4_vals(void* y, int64_t N, int64_t m, int64_t n0, const float (&v)[4],
-                                           bool vec_ok) {
-    if (kYbf16) {
+                                           bool vec_ok, const QScale& q) {
+    if (kOut == kOutBF16) {
         uint16_t* yr = (uint16_t*)y + m * N;
         if (vec_ok && n0 + 3 < N) {
             uint2 o;
@@ -129,6 +145,16 @@ __device__ __forceinline__ void store4_vals(void* y, int64_t N, int64_t m, int64
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (n0 + r < N) yr[n0 + r] = (uint16_t)(pack_bf16x2(v[r], 0.0f) & 0xFFFFu);
+        }
+    } else if (kOut == kOutE4M3) {
+        uint8_t* yr = (uint8_t*)y + m * N;
+        const uint32_t c = out_codes4(v[0], v[1], v[2], v[3], q);
+        if (vec_ok && n0 + 3 < N) {
+            *reinterpret_cast<uint32_t*>(yr + n0) = c;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n0 + r < N) yr[n0 + r] = (uint8_t)((c >> (8 * r)) & 0xFFu);
         }
     } else {
         float* yr = (float*)y + m * N;
@@ -161,12 +187,12 @@ __device__ __forceinline__ void store4_vals(void* y, int64_t N, int64_t m, int64
 // Each k block's 16 x 16 partial products start from zero, are multiplied by
 // s_a[m, kb] * s_w[n / 128, kb] and added to the fp32 accumulator, so the
 // epilogue only rounds.  A 16-row subtile never straddles a 128-row block.
-template <bool kFp8, bool kYbf16, int kMT, int kNS, int kKS, int kDepth, bool kWPacked, bool kAPacked,
+template <bool kFp8, int kOut, int kMT, int kNS, int kKS, int kDepth, bool kWPacked, bool kAPacked,
           bool kBlock = false>
 __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                         int sa_per_token, const uint8_t* __restrict__ W,
                                                         const float* __restrict__ sw, void* __restrict__ Y, int M,
-                                                        int N, int K) {
+                                                        int N, int K, const float* __restrict__ qs) {
     __shared__ f32x4 red[kKS > 1 ? kKS - 1 : 1][kNS * kMT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n_base = (int64_t)blockIdx.x * (16 * kNS);
@@ -278,6 +304,7 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
     }
     if (wave == 0) {
         const bool vec_ok = (N & 3) == 0;
+        const QScale q = out_qscale<kOut>(qs);
 #pragma unroll
         for (int s = 0; s < kNS; ++s)
 #pragma unroll
@@ -288,8 +315,8 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
                 const int m = 16 * t + r16;
                 const int64_t n0 = n_base + 16 * s + 4 * (lane >> 4);
                 if (m < M && n0 < N) {
-                    if (kBlock) store4_raw<kYbf16>(Y, N, m, n0, v, vec_ok);
-                    else store4<kYbf16>(Y, N, m, n0, v, sa[sa_per_token ? m : 0], sw, vec_ok);
+                    if (kBlock) store4_raw<kOut>(Y, N, m, n0, v, vec_ok, q);
+                    else store4<kOut>(Y, N, m, n0, v, sa[sa_per_token ? m : 0], sw, vec_ok, q);
                 }
             }
     }
@@ -478,6 +505,42 @@ __device__ __forceinline__ void epi_store(const uint8_t* wl, uint16_t* __restric
     }
 }
 
+// The same staging for E4M3 output: 128-byte rows, the 16-byte slots of a row
+// XORed with the row's low three bits; one store instruction covers eight rows.
+constexpr int kEpiQRowBytes = 128;
+
+__device__ __forceinline__ uint32_t epi_q_offset(int row, int col) {
+    return (uint32_t)(row * kEpiQRowBytes + (col ^ ((row & 7) << 4)));
+}
+
+__device__ __forceinline__ void epi_put4_q(uint8_t* wl, int row, int col, uint32_t codes) {
+    *reinterpret_cast<uint32_t*>(wl + epi_q_offset(row, col)) = codes;
+}
+
+template <int kRows>
+__device__ __forceinline__ void epi_store_q(const uint8_t* wl, uint8_t* __restrict__ Y, int64_t M, int64_t N,
+                                            int64_t m0, int64_t n0, int lane) {
+    const int c = lane & 7;
+    const int64_t n = n0 + 16 * c;
+    const bool vec = (N & 15) == 0 && n + 16 <= N;
+#pragma unroll 4
+    for (int it = 0; it < kRows / 8; ++it) {
+        const int row = 8 * it + (lane >> 3);
+        const int64_t m = m0 + row;
+        if (m >= M) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(wl + epi_q_offset(row, 16 * c));
+        uint8_t* yr = Y + m * N;
+        if (vec) {
+            *reinterpret_cast<uint4*>(yr + n) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (n + e < N) yr[n + e] = (uint8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        }
+    }
+}
+
 // The four per-channel scales of columns n0 .. n0 + 3 (0 past N).
 __device__ __forceinline__ void load_sw4(const float* __restrict__ sw, int64_t N, int64_t n0, float (&v)[4]) {
 #pragma unroll
@@ -496,11 +559,11 @@ __device__ __forceinline__ void load_sw4(const float* __restrict__ sw, int64_t N
 // step kb the wave waits for its copies of block kb only (vmcnt(16): the 16
 // copies of block kb + 1 stay in flight).  Past the last block the copies
 // repeat block nkb - 1, so the loop body has no branch.
-template <bool kYbf16, bool kWPacked, bool kAPacked>
+template <int kOut, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                        int sa_per_token, const uint8_t* __restrict__ W,
                                                        const float* __restrict__ sw, void* __restrict__ Y, int M,
-                                                       int N, int K, int tiles_per_xcd) {
+                                                       int N, int K, int tiles_per_xcd, const float* __restrict__ qs) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages x (A 32 KB + W 32 KB)
     constexpr int kStage = 32 * kPackBlock;
     const int lane = threadIdx.x & 63;
@@ -540,10 +603,11 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
         const uint8_t* la = cur + wm * 8 * kPackBlock;
         const uint8_t* lw = cur + (16 + wn * 8) * kPackBlock;
         Frag wf[8], af[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) wf[i] = load_frag_packed(lw + i * kPackBlock, lane);
+        // A fragments first: the first row of multiplies needs all of them and W fragment 0
 #pragma unroll
         for (int j = 0; j < 8; ++j) af[j] = load_frag_packed(la + j * kPackBlock, lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wf[i] = load_frag_packed(lw + i * kPackBlock, lane);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[0][j] = mma_fp8(wf[0], af[j], acc[0][j]);
         __builtin_amdgcn_sched_barrier(0);   // the first row of multiplies overlaps the remaining reads
@@ -566,9 +630,10 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
 
-    if (kYbf16) {
+    if (kOut == kOutBF16 || kOut == kOutE4M3) {
         __syncthreads();  // every wave is done with the stages: the LDS now holds the output tiles
         uint8_t* wl = smem + wave * kEpiWaveBytes;
+        const QScale q = out_qscale<kOut>(qs);
         float sam[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -583,15 +648,20 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const f32x4 a = acc[i][j];
-                epi_put4(wl, 16 * j + (lane & 15), 16 * i + 4 * (lane >> 4), (a[0] * sam[j]) * s4[0],
-                         (a[1] * sam[j]) * s4[1], (a[2] * sam[j]) * s4[2], (a[3] * sam[j]) * s4[3]);
+                const int row = 16 * j + (lane & 15), col = 16 * i + 4 * (lane >> 4);
+                const float v0 = (a[0] * sam[j]) * s4[0], v1 = (a[1] * sam[j]) * s4[1];
+                const float v2 = (a[2] * sam[j]) * s4[2], v3 = (a[3] * sam[j]) * s4[3];
+                if (kOut == kOutBF16) epi_put4(wl, row, col, v0, v1, v2, v3);
+                else epi_put4_q(wl, row, col, out_codes4(v0, v1, v2, v3, q));
             }
         }
         __syncthreads();
-        epi_store(wl, (uint16_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
+        if (kOut == kOutBF16) epi_store(wl, (uint16_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
+        else epi_store_q<128>(wl, (uint8_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
         return;
     }
     const bool vec_ok = (N & 3) == 0;
+    const QScale q = out_qscale<kOut>(qs);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int64_t m = m_base + wm * 128 + 16 * j + (lane & 15);
@@ -600,7 +670,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t n0 = n_base + wn * 128 + 16 * i + 4 * (lane >> 4);
-            if (n0 < N) store4<kYbf16>(Y, N, m, n0, acc[i][j], sam, sw, vec_ok);
+            if (n0 < N) store4<kOut>(Y, N, m, n0, acc[i][j], sam, sw, vec_ok, q);
         }
     }
 }
@@ -618,11 +688,12 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
 // row's 16-row subtile holds in the 16 x 16 fragment order of LDS; A and W use
 // the same assignment, so every product pairs matching k.  Output lane layout:
 // acc[r] of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of the tile.
-template <bool kYbf16, bool kWPacked, bool kAPacked>
+template <int kOut, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                          int sa_per_token, const uint8_t* __restrict__ W,
                                                          const float* __restrict__ sw, void* __restrict__ Y, int M,
-                                                         int N, int K, int tiles_per_xcd) {
+                                                         int N, int K, int tiles_per_xcd,
+                                                         const float* __restrict__ qs) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages x (A 32 KB + W 32 KB)
     constexpr int kStage = 32 * kPackBlock;
     const int lane = threadIdx.x & 63;
@@ -710,9 +781,10 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
 
-    if (kYbf16) {
+    if (kOut == kOutBF16 || kOut == kOutE4M3) {
         __syncthreads();  // every wave is done with the stages: the LDS now holds the output tiles
         uint8_t* wl = smem + wave * kEpiWaveBytes;
+        const QScale q = out_qscale<kOut>(qs);
         float sam[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -730,16 +802,20 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const f32x16 a = acc[i][j];
-                    epi_put4(wl, 32 * j + (lane & 31), col, (a[4 * g] * sam[j]) * s4[0],
-                             (a[4 * g + 1] * sam[j]) * s4[1], (a[4 * g + 2] * sam[j]) * s4[2],
-                             (a[4 * g + 3] * sam[j]) * s4[3]);
+                    const int row = 32 * j + (lane & 31);
+                    const float v0 = (a[4 * g] * sam[j]) * s4[0], v1 = (a[4 * g + 1] * sam[j]) * s4[1];
+                    const float v2 = (a[4 * g + 2] * sam[j]) * s4[2], v3 = (a[4 * g + 3] * sam[j]) * s4[3];
+                    if (kOut == kOutBF16) epi_put4(wl, row, col, v0, v1, v2, v3);
+                    else epi_put4_q(wl, row, col, out_codes4(v0, v1, v2, v3, q));
                 }
             }
         __syncthreads();
-        epi_store(wl, (uint16_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
+        if (kOut == kOutBF16) epi_store(wl, (uint16_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
+        else epi_store_q<128>(wl, (uint8_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
         return;
     }
     const bool vec_ok = (N & 3) == 0;
+    const QScale q = out_qscale<kOut>(qs);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t m = m_base + wm * 128 + 32 * j + (lane & 31);
@@ -751,7 +827,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
             for (int g = 0; g < 4; ++g) {
                 const int64_t n0 = n_base + wn * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
                 const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                if (n0 < N) store4<kYbf16>(Y, N, m, n0, v, sam, sw, vec_ok);
+                if (n0 < N) store4<kOut>(Y, N, m, n0, v, sam, sw, vec_ok, q);
             }
     }
 }
@@ -797,12 +873,13 @@ __device__ __forceinline__ void copy4_to_lds(const float* src, uint32_t lds_addr
         : "memory", "m0");
 }
 
-template <bool kYbf16, bool kWPacked, bool kAPacked>
+template <int kOut, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __restrict__ A,
                                                              const float* __restrict__ sa,
                                                              const uint8_t* __restrict__ W,
                                                              const float* __restrict__ sw, void* __restrict__ Y,
-                                                             int M, int N, int K, int tiles_per_xcd) {
+                                                             int M, int N, int K, int tiles_per_xcd,
+                                                             const float* __restrict__ qs) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages of kBwStage
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -897,7 +974,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
 
-    if (kYbf16) {
+    static_assert(kOut != kOutE4M3, "block-wise GEMMs write bf16 or fp32");
+    const QScale q = out_qscale<kOut>(qs);
+    if (kOut == kOutBF16) {
         __syncthreads();  // every wave is done with the stages: the LDS now holds the output tiles
         uint8_t* wl = smem + wave * (kEpiWaveBytes / 2);
 #pragma unroll
@@ -919,87 +998,93 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t n0 = n_base + wn * 128 + 16 * i + 4 * (lane >> 4);
-            if (n0 < N) store4_raw<kYbf16>(Y, N, m, n0, acc[i][j], vec_ok);
+            if (n0 < N) store4_raw<kOut>(Y, N, m, n0, acc[i][j], vec_ok, q);
         }
     }
 }
 static_assert(8 * (kEpiWaveBytes / 2) <= 2 * kBwStage, "the staged output reuses the two operand stages");
 
-template <bool kFp8, bool kYbf16, bool kWPacked, bool kAPacked, int kMT, int kNS, int kKS, int kDepth>
+template <bool kFp8, int kOut, bool kWPacked, bool kAPacked, int kMT, int kNS, int kKS, int kDepth>
 static void launch_skinny(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw, void* y,
-                          int M, int N, int K, hipStream_t stream) {
+                          int M, int N, int K, const float* qs, hipStream_t stream) {
     dim3 grid((unsigned)((N + 16 * kNS - 1) / (16 * kNS))), block(64 * kKS);
-    gemm_skinny<kFp8, kYbf16, kMT, kNS, kKS, kDepth, kWPacked, kAPacked>
-        <<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K);
+    gemm_skinny<kFp8, kOut, kMT, kNS, kKS, kDepth, kWPacked, kAPacked>
+        <<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, qs);
 }
 
-template <bool kFp8, bool kYbf16, bool kWPacked, bool kAPacked>
+template <bool kFp8, int kOut, bool kWPacked, bool kAPacked>
 static hipError_t launch_gemm_t(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw,
-                                void* y, int M, int N, int K, hipStream_t stream) {
+                                void* y, int M, int N, int K, const float* qs, hipStream_t stream) {
     if (M <= 16) {
-        launch_skinny<kFp8, kYbf16, kWPacked, kAPacked, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw,
-                                                                                               y, M, N, K, stream);
+        launch_skinny<kFp8, kOut, kWPacked, kAPacked, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y,
+                                                                                             M, N, K, qs, stream);
     } else if (M <= 32) {
-        launch_skinny<kFp8, kYbf16, kWPacked, kAPacked, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw,
-                                                                                               y, M, N, K, stream);
+        launch_skinny<kFp8, kOut, kWPacked, kAPacked, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y,
+                                                                                             M, N, K, qs, stream);
     } else {
         const int tiles = ((M + kBig - 1) / kBig) * ((N + kBig - 1) / kBig);
         const int per = (tiles + 7) / 8;
         dim3 grid((unsigned)(per * 8)), block(256);
         if (kFp8)
-            gemm_big_fp8<kYbf16, kWPacked, kAPacked>
-                <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per);
+            gemm_big_fp8<kOut, kWPacked, kAPacked>
+                <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per, qs);
         else
-            gemm_big_exact<kYbf16, kWPacked, kAPacked>
-                <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per);
+            gemm_big_exact<kOut, kWPacked, kAPacked>
+                <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per, qs);
     }
     return hipGetLastError();
 }
 
 template <bool kFp8, bool kWPacked, bool kAPacked>
 static hipError_t launch_gemm_y(const uint8_t* aq, const float* sa, int pt, const uint8_t* wq, const float* sw, void* y,
-                                bool y_bf16, int M, int N, int K, hipStream_t stream) {
-    return y_bf16 ? launch_gemm_t<kFp8, true, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, stream)
-                  : launch_gemm_t<kFp8, false, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, stream);
+                                int out_kind, int M, int N, int K, const float* qs, hipStream_t stream) {
+    if (out_kind == kOutBF16)
+        return launch_gemm_t<kFp8, kOutBF16, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, qs, stream);
+    if (out_kind == kOutE4M3)
+        return launch_gemm_t<kFp8, kOutE4M3, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, qs, stream);
+    return launch_gemm_t<kFp8, kOutF32, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, qs, stream);
 }
 
 template <bool kFp8>
 static hipError_t launch_gemm_m(const uint8_t* aq, bool a_packed, const float* sa, int pt, const uint8_t* wq,
-                                bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
-                                hipStream_t stream) {
+                                bool w_packed, const float* sw, void* y, int out_kind, int M, int N, int K,
+                                const float* qs, hipStream_t stream) {
     if (a_packed)
-        return w_packed ? launch_gemm_y<kFp8, true, true>(aq, sa, pt, wq, sw, y, y_bf16, M, N, K, stream)
-                        : launch_gemm_y<kFp8, false, true>(aq, sa, pt, wq, sw, y, y_bf16, M, N, K, stream);
-    return w_packed ? launch_gemm_y<kFp8, true, false>(aq, sa, pt, wq, sw, y, y_bf16, M, N, K, stream)
-                    : launch_gemm_y<kFp8, false, false>(aq, sa, pt, wq, sw, y, y_bf16, M, N, K, stream);
+        return w_packed ? launch_gemm_y<kFp8, true, true>(aq, sa, pt, wq, sw, y, out_kind, M, N, K, qs, stream)
+                        : launch_gemm_y<kFp8, false, true>(aq, sa, pt, wq, sw, y, out_kind, M, N, K, qs, stream);
+    return w_packed ? launch_gemm_y<kFp8, true, false>(aq, sa, pt, wq, sw, y, out_kind, M, N, K, qs, stream)
+                    : launch_gemm_y<kFp8, false, false>(aq, sa, pt, wq, sw, y, out_kind, M, N, K, qs, stream);
 }
 
 hipError_t launch_gemm(const uint8_t* aq, bool a_packed, const float* a_scales, bool a_per_token, const uint8_t* wq,
-                       bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
-                       bool fp8_mfma, hipStream_t stream) {
+                       bool w_packed, const float* w_scales, void* y, int out_kind, const float* out_scale, int64_t M,
+                       int64_t N, int64_t K, bool fp8_mfma, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const int pt = a_per_token ? 1 : 0;
     const int m = (int)M, n = (int)N, k = (int)K;
-    if (fp8_mfma) return launch_gemm_m<true>(aq, a_packed, a_scales, pt, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
-    return launch_gemm_m<false>(aq, a_packed, a_scales, pt, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
+    if (fp8_mfma)
+        return launch_gemm_m<true>(aq, a_packed, a_scales, pt, wq, w_packed, w_scales, y, out_kind, m, n, k, out_scale,
+                                   stream);
+    return launch_gemm_m<false>(aq, a_packed, a_scales, pt, wq, w_packed, w_scales, y, out_kind, m, n, k, out_scale,
+                                stream);
 }
 
-template <bool kFp8, bool kYbf16, bool kWPacked, bool kAPacked>
+template <bool kFp8, int kOut, bool kWPacked, bool kAPacked>
 static hipError_t launch_blockwise_t(const uint8_t* aq, const float* sa, const uint8_t* wq, const float* sw, void* y,
                                      int M, int N, int K, hipStream_t stream) {
     dim3 block(64 * SKINNY_KS);
     dim3 grid((unsigned)((N + 16 * SKINNY_NS - 1) / (16 * SKINNY_NS)));
     if (M <= 16) {
-        gemm_skinny<kFp8, kYbf16, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
-            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K);
+        gemm_skinny<kFp8, kOut, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
+            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K, nullptr);
     } else if (M <= 32) {
-        gemm_skinny<kFp8, kYbf16, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
-            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K);
+        gemm_skinny<kFp8, kOut, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
+            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K, nullptr);
     } else if (kFp8) {
         const int tiles = ((M + kBig - 1) / kBig) * ((N + kBig - 1) / kBig);
         const int per = (tiles + 7) / 8;
-        gemm_big_blockwise<kYbf16, kWPacked, kAPacked>
-            <<<dim3((unsigned)(per * 8)), dim3(512), 2 * kBwStage, stream>>>(aq, sa, wq, sw, y, M, N, K, per);
+        gemm_big_blockwise<kOut, kWPacked, kAPacked>
+            <<<dim3((unsigned)(per * 8)), dim3(512), 2 * kBwStage, stream>>>(aq, sa, wq, sw, y, M, N, K, per, nullptr);
     } else {
         return hipErrorInvalidValue;  // exact block-wise accumulation exists for M <= 32 only (checked by the ABI)
     }
@@ -1010,7 +1095,8 @@ template <bool kFp8>
 static hipError_t launch_blockwise_m(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq,
                                      bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
                                      hipStream_t stream) {
-#define FP8SG_BW(YB, WP, AP) launch_blockwise_t<kFp8, YB, WP, AP>(aq, sa, wq, sw, y, M, N, K, stream)
+#define FP8SG_BW(YB, WP, AP) \
+    launch_blockwise_t<kFp8, (YB) ? kOutBF16 : kOutF32, WP, AP>(aq, sa, wq, sw, y, M, N, K, stream)
     if (y_bf16) {
         if (a_packed) return w_packed ? FP8SG_BW(true, true, true) : FP8SG_BW(true, false, true);
         return w_packed ? FP8SG_BW(true, true, false) : FP8SG_BW(true, false, false);
@@ -1061,10 +1147,10 @@ __device__ __forceinline__ Frag load_frag_lds(const uint8_t* p) {
     return f;
 }
 
-template <bool kFp8, bool kYbf16, bool kWPacked, int kNS, int kKS, int kM>
+template <bool kFp8, int kOut, bool kWPacked, int kNS, int kKS, int kM>
 __global__ __launch_bounds__(64 * kKS) __attribute__((amdgpu_waves_per_eu(4))) void gemm_skinny_fused(
     const uint16_t* __restrict__ X, float* __restrict__ sa_out, const uint8_t* __restrict__ W,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, const float* __restrict__ qs) {
     extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];  // [M][K + 16] codes
     __shared__ f32x4 red[kKS > 1 ? kKS - 1 : 1][kNS][64];
     __shared__ float row_max[kKS][kFusedMaxM];
@@ -1190,6 +1276,7 @@ __global__ __launch_bounds__(64 * kKS) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     if (wave == 0) {
         const bool vec_ok = (N & 3) == 0;
+        const QScale q = out_qscale<kOut>(qs);
         const int m = r16;
 #pragma unroll
         for (int s = 0; s < kNS; ++s) {
@@ -1197,23 +1284,30 @@ __global__ __launch_bounds__(64 * kKS) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
             for (int w = 0; w < kKS - 1; ++w) a += red[w][s][lane];
             const int64_t n0 = n_base + 16 * s + 4 * (lane >> 4);
-            if (m < M && n0 < N) store4<kYbf16>(Y, N, m, n0, a, row_scale[m], sw, vec_ok);
+            if (m < M && n0 < N) store4<kOut>(Y, N, m, n0, a, row_scale[m], sw, vec_ok, q);
         }
     }
 }
 
-template <bool kFp8, bool kYbf16, bool kWPacked>
+template <bool kFp8, int kOut, bool kWPacked>
 static void launch_fused_t(const uint16_t* x, float* sa_out, const uint8_t* wq, const float* sw, void* y, int M,
-                           int N, int K, hipStream_t stream) {
+                           int N, int K, const float* qs, hipStream_t stream) {
     dim3 grid((unsigned)((N + 16 * SKINNY_NS - 1) / (16 * SKINNY_NS))), block(64 * kFusedKS);
     const size_t lds = (size_t)M * (size_t)(K + 16);
 #define FP8SG_FUSED_M(KM) \
-    gemm_skinny_fused<kFp8, kYbf16, kWPacked, SKINNY_NS, kFusedKS, KM><<<grid, block, lds, stream>>>(x, sa_out, wq, sw, \
-                                                                                                  y, M, N, K)
+    gemm_skinny_fused<kFp8, kOut, kWPacked, SKINNY_NS, kFusedKS, KM><<<grid, block, lds, stream>>>(x, sa_out, wq, sw, \
+                                                                                                y, M, N, K, qs)
     if (M <= 1) FP8SG_FUSED_M(1);
     else if (M <= 2) FP8SG_FUSED_M(2);
     else FP8SG_FUSED_M(4);
 #undef FP8SG_FUSED_M
+}
+
+template <bool kFp8, int kOut>
+static void launch_fused_w(const uint16_t* x, float* sa_out, const uint8_t* wq, bool w_packed, const float* sw,
+                           void* y, int M, int N, int K, const float* qs, hipStream_t stream) {
+    if (w_packed) launch_fused_t<kFp8, kOut, true>(x, sa_out, wq, sw, y, M, N, K, qs, stream);
+    else launch_fused_t<kFp8, kOut, false>(x, sa_out, wq, sw, y, M, N, K, qs, stream);
 }
 
 bool gemm_fused_quant_fits(bool x_is_bf16, int64_t M, int64_t K) {
@@ -1222,17 +1316,19 @@ bool gemm_fused_quant_fits(bool x_is_bf16, int64_t M, int64_t K) {
 }
 
 hipError_t launch_gemm_fused_quant(const uint16_t* x, float* sa_out, const uint8_t* wq, bool w_packed,
-                                   const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
-                                   bool fp8_mfma, hipStream_t stream) {
+                                   const float* w_scales, void* y, int out_kind, const float* out_scale, int64_t M,
+                                   int64_t N, int64_t K, bool fp8_mfma, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const int m = (int)M, n = (int)N, k = (int)K;
-#define FP8SG_FUSED(F8, YB, WP) launch_fused_t<F8, YB, WP>(x, sa_out, wq, w_scales, y, m, n, k, stream)
+#define FP8SG_FUSED(F8, OUT) launch_fused_w<F8, OUT>(x, sa_out, wq, w_packed, w_scales, y, m, n, k, out_scale, stream)
     if (fp8_mfma) {
-        if (y_bf16) w_packed ? FP8SG_FUSED(true, true, true) : FP8SG_FUSED(true, true, false);
-        else w_packed ? FP8SG_FUSED(true, false, true) : FP8SG_FUSED(true, false, false);
+        if (out_kind == kOutBF16) FP8SG_FUSED(true, kOutBF16);
+        else if (out_kind == kOutE4M3) FP8SG_FUSED(true, kOutE4M3);
+        else FP8SG_FUSED(true, kOutF32);
     } else {
-        if (y_bf16) w_packed ? FP8SG_FUSED(false, true, true) : FP8SG_FUSED(false, true, false);
-        else w_packed ? FP8SG_FUSED(false, false, true) : FP8SG_FUSED(false, false, false);
+        if (out_kind == kOutBF16) FP8SG_FUSED(false, kOutBF16);
+        else if (out_kind == kOutE4M3) FP8SG_FUSED(false, kOutE4M3);
+        else FP8SG_FUSED(false, kOutF32);
     }
 #undef FP8SG_FUSED
     return hipGetLastError();

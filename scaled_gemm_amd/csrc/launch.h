@@ -8,6 +8,10 @@
 
 namespace fp8sg {
 
+// What the GEMM kernels write: fp32, bf16, or E4M3 codes of the fp32 result
+// under a given per-tensor output scale.
+constexpr int kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2;
+
 // packed: write the codes in the GEMM fragment order (K % 128 == 0) instead of [M, K].
 hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
                             bool packed, hipStream_t stream);
@@ -27,15 +31,15 @@ hipError_t launch_grouped_quant(const void* x, bool x_is_bf16, int64_t numel, co
                                 int64_t inner_units, int nscales, int fmt, uint8_t* q, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t* aq, bool a_packed, const float* a_scales, bool a_per_token, const uint8_t* wq,
-                       bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
-                       bool fp8_mfma, hipStream_t stream);
+                       bool w_packed, const float* w_scales, void* y, int out_kind, const float* out_scale, int64_t M,
+                       int64_t N, int64_t K, bool fp8_mfma, hipStream_t stream);
 
 // Decode GEMM with the per-token activation quantization inside the same
 // kernel (bf16 X), for the shapes gemm_fused_quant_fits accepts.  sa_out may be NULL.
 bool gemm_fused_quant_fits(bool x_is_bf16, int64_t M, int64_t K);
 hipError_t launch_gemm_fused_quant(const uint16_t* x, float* sa_out, const uint8_t* wq, bool w_packed,
-                                   const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
-                                   bool fp8_mfma, hipStream_t stream);
+                                   const float* w_scales, void* y, int out_kind, const float* out_scale, int64_t M,
+                                   int64_t N, int64_t K, bool fp8_mfma, hipStream_t stream);
 
 // Block-wise scaled GEMM: a_scales [M, K/128], w_scales [ceil(N/128), K/128].
 hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* a_scales, const uint8_t* wq,

@@ -57,6 +57,8 @@ _SIGS = {
     "fp8_pack_weights": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _sz,
                                _vp]),
+    "fp8_scaled_gemm_fp8out": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp,
+                                      _sz, _vp]),
     "fp8_quant_per_token_group": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]),
     "fp8_quant_weight_blockwise": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_blockwise": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
@@ -188,10 +190,8 @@ def fp8_scaled_gemm_workspace_size(a_dtype, a_scale_mode, M: int, N: int, K: int
     return int(lib().fp8_scaled_gemm_workspace_size(code, _SCALE[a_scale_mode], M, N, K))
 
 
-def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor, w_scales: torch.Tensor, *,
-                    a_scale_mode="per_token", out_dtype=torch.bfloat16, accum="exact", w_layout="row_major",
-                    a_layout="row_major", a_shape: Optional[tuple] = None, y: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor, w_scales: torch.Tensor,
+                    **kw) -> torch.Tensor:
     """Y [M, N] = diag(s_a) (A_q W_q^T) diag(s_w).
 
     a: uint8 E4M3 codes [M, K] (a_scales is then an input), or bf16/fp32
@@ -200,8 +200,18 @@ def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch
     a_layout="packed": a is the 1-D fragment-order buffer of fp8_pack_weights
     applied to the [M, K] codes, and a_shape=(M, K) gives the shape.
     wq: [N, K] row-major codes, or (w_layout="packed") the 1-D buffer of
-    fp8_pack_weights; N is taken from w_scales.
+    fp8_pack_weights; N is taken from w_scales.  Keywords: a_scale_mode,
+    out_dtype, accum, w_layout, a_layout, a_shape, y, workspace, stream.
     """
+    return _scaled_gemm(a, a_scales, wq, w_scales, **kw)
+
+
+def _scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor, w_scales: torch.Tensor, *,
+                 a_scale_mode="per_token", out_dtype=torch.bfloat16, accum="exact", w_layout="row_major",
+                 a_layout="row_major", a_shape: Optional[tuple] = None, y: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """Shared body of fp8_scaled_gemm and fp8_scaled_gemm_fp8out (out_scale given)."""
     _need(a, "a", (torch.uint8, torch.bfloat16, torch.float32))
     _need(wq, "wq", (torch.uint8,))
     _need(w_scales, "w_scales", (torch.float32,))
@@ -225,17 +235,32 @@ def fp8_scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch
     if a_scales is not None:
         _need(a_scales, "a_scales", (torch.float32,), (M,) if mode == SCALE_PER_TOKEN else (1,))
     a_code = {torch.uint8: E4M3, torch.bfloat16: BF16, torch.float32: F32}[a.dtype]
-    y_code = {torch.bfloat16: BF16, torch.float32: F32}[out_dtype]
+    if out_scale is not None:
+        out_dtype = torch.uint8
+    y_code = {torch.bfloat16: BF16, torch.float32: F32, torch.uint8: E4M3}[out_dtype]
     y = torch.empty((M, N), dtype=out_dtype, device=a.device) if y is None else y
     _need(y, "y", (out_dtype,), (M, N))
     need = int(lib().fp8_scaled_gemm_workspace_size(a_code, mode, M, N, K))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out_scale is not None:
+        _need(out_scale, "out_scale", (torch.float32,), (1,))
+        _check(lib().fp8_scaled_gemm_fp8out(_ptr(a), a_code, _ptr(a_scales), mode, _ptr(wq), layout, _ptr(w_scales),
+                                            _ptr(out_scale), _ptr(y), M, N, K, _ACCUM[accum], _ptr(workspace),
+                                            ws_bytes, _stream(stream)), "fp8_scaled_gemm_fp8out")
+        return y
     _check(lib().fp8_scaled_gemm(_ptr(a), a_code, _ptr(a_scales), mode, _ptr(wq), layout, _ptr(w_scales), _ptr(y),
                                  y_code, M, N, K, _ACCUM[accum], _ptr(workspace), ws_bytes, _stream(stream)),
            "fp8_scaled_gemm")
     return y
+
+
+def fp8_scaled_gemm_fp8out(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor,
+                           w_scales: torch.Tensor, out_scale: torch.Tensor, **kw) -> torch.Tensor:
+    """fp8_scaled_gemm with E4M3 output codes [M, N] (uint8) under the per-tensor
+    output scale out_scale [1]: code = E4M3(RN32(y32 / out_scale)), saturating."""
+    return _scaled_gemm(a, a_scales, wq, w_scales, out_scale=out_scale, **kw)
 
 
 def fp8_quant_per_token_group(x: torch.Tensor, layout="row_major", q: Optional[torch.Tensor] = None,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     names = sg.declared_symbols()
-    assert len(names) == 16
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
     missing = [n for n in names if n not in exported]
@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert sg.lib().fp8sg_version() == 4
+    assert sg.lib().fp8sg_version() == 5
     for st in range(8):
         assert sg.status_string(st)
     assert sg.status_string(99) == "unknown status"
