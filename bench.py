@@ -65,7 +65,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--quick", action="store_true", help="headline only: skip the detail workloads")
     ap.add_argument("--workload", nargs="*", default=None,
-                    help="detail workloads to run (default all): prefill large quant kv weights blockwise")
+                    help="detail workloads to run (default all): prefill large quant kv weights blockwise fp8out")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -199,7 +199,8 @@ def main():
                 "timing": "HIP events around 100 back-to-back launches on the library's stream, mean of 5"}
 
     # ------------------------------------------------------------ details
-    wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights", "blockwise"}
+    wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights", "blockwise",
+                                                       "fp8out"}
     if args.quick:
         wanted = set()
     del wqs[1:], wrm[1:]
@@ -434,6 +435,45 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
                         "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
             del xl, aq, sa, wq, wp, y
             torch.cuda.empty_cache()
+
+    if "fp8out" in wanted:
+        log("fp8 output epilogue")
+        from workloads import decode_inputs
+        # decode M = 32 and the K = 4096 prefill GEMM with E4M3 output codes
+        # (per-tensor output scale), beside the same call with bf16 output
+        _, w, _ = decode_inputs(1)
+        wq, sw = sg.fp8_quant_weight_per_channel(torch.from_numpy(w).to(dev))
+        wps = copies(sg.fp8_pack_weights(wq), 8)
+        N, K = w.shape
+        xb, _, _ = decode_inputs(32, with_weight=False)
+        aq, sa = sg.fp8_quant_per_token(to_bf16(xb))
+        ap = sg.fp8_pack_weights(aq)
+        so = torch.tensor([0.05], dtype=torch.float32, device=dev)
+        yq = torch.empty((32, N), dtype=torch.uint8, device=dev)
+        d = timed_events(lambda i: sg.fp8_scaled_gemm_fp8out(ap, sa, wps[i % 8], sw, so, y=yq, w_layout="packed",
+                                                             a_layout="packed", a_shape=(32, K)), 100, 20)
+        kb = N * K + 4 * N + 32 * K + 4 * 32 + 32 * N
+        out.append({"workload": f"decode GEMM kernel M=32 N={N} K={K}, E4M3 output (pre-quantized A)",
+                    "accum": "exact", "avg_us": round(float(d.mean()) * 1e3, 2), "GB_s": _gbs(kb, d.mean()),
+                    "frac_hbm": round(_gbs(kb, d.mean()) / HBM_PEAK_GBS, 4)})
+        del wps, wq, aq, ap
+        xb, w, _ = prefill_inputs(4096)
+        M, N = xb.shape[0], w.shape[0]
+        aq, sa = sg.fp8_quant_per_token(to_bf16(xb))
+        ap = sg.fp8_pack_weights(aq)
+        wq, sw = sg.fp8_quant_weight_per_channel(torch.from_numpy(w).to(dev))
+        wp = sg.fp8_pack_weights(wq)
+        yq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        for accum in ("mfma_fp8", "exact"):
+            d = timed_events(lambda i: sg.fp8_scaled_gemm_fp8out(ap, sa, wp, sw, so, y=yq, accum=accum,
+                                                                 w_layout="packed", a_layout="packed",
+                                                                 a_shape=(M, 4096)), 10, 3, reps=3)
+            tf = _tflops(2.0 * M * N * 4096, d.mean())
+            out.append({"workload": f"prefill GEMM {M}x{N}x4096, E4M3 output (pre-quantized A)", "accum": accum,
+                        "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
+                        "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
+        del aq, ap, wq, wp, yq
+        torch.cuda.empty_cache()
 
     if "kv" in wanted:
         log("kv cache")

@@ -205,10 +205,10 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
  * Scaled GEMM with an FP8 output epilogue: the result is written as the E4M3
  * input of a next layer that takes a static per-tensor activation scale, so no
  * separate quantization pass reads Y again (FP8 Inference Explained, in depth
- * -- "Scales and their granularity": engines fold the activation quantization
- * into the kernel that produces the activation; Quantization: FP8 inference and
- * KV-cache quantization -- "Dynamic scales or static scales": a static scale
- * costs nothing at run time, values beyond it saturate).
+ * -- "Scales and their granularity": engines fuse the activation quantization
+ * work into the preceding kernel, and static activation scales cost nothing at
+ * run time; Quantization: FP8 inference and KV-cache quantization -- "Dynamic
+ * scales or static scales": values beyond a static scale saturate).
  *   All arguments as for fp8_scaled_gemm, except:
  *   out_scale  [1] fp32 (device), the per-tensor scale of the output codes,
  *              positive and finite
@@ -315,6 +315,42 @@ fp8sg_status fp8_kv_dequant(const uint8_t* kvq, int64_t B, int64_t S, int64_t H,
 fp8sg_status fp8_kv_append(const uint16_t* kv_new, const int32_t* pos, int64_t B, int64_t S_cap,
                            int64_t H, int64_t D, const float* head_scales, int fmt,
                            uint8_t* cache, void* stream);
+
+/*
+ * Bytes of device workspace fp8_kv_decode_attention needs (the per-chunk
+ * partial results).  Host-only; no HIP call.
+ */
+size_t fp8_kv_decode_attention_workspace_size(int64_t B, int64_t S_cap, int64_t Hq, int64_t Hkv, int64_t D);
+
+/*
+ * One decode step of attention over an FP8 KV cache: query q[b, h, :] attends
+ * over positions 0 .. lengths[b] - 1 of kv head g = h / (Hq / Hkv) (grouped
+ * query heads).  The cache is read back as code value times the head's scale
+ * and the attention is computed in fp32 (FP8 Inference Explained, in depth --
+ * "FP8 KV cache": per-attention-head scales; backends that do not compute in
+ * FP8 read the cache back and compute in higher precision), with the softmax
+ * taken block by block by the online recurrence ("FlashAttention v1/v2/v3/v4"
+ * post -- "The trick that made it all possible: online softmax"):
+ *     s_t = scale * q . (dec(K_t) s_K[g]),  p = softmax(s),  o = sum_t p_t dec(V_t) s_V[g].
+ *   q           [B, Hq, D] bf16
+ *   k_cache,
+ *   v_cache     [B, S_cap, Hkv, D] codes of format fmt (FP8SG_E4M3 or FP8SG_E5M2),
+ *               as written by fp8_kv_quant / fp8_kv_append
+ *   k_scales,
+ *   v_scales    [Hkv] fp32 per-head scales
+ *   lengths     [B] int32 (device): positions attended per sequence; values are
+ *               clamped to [0, S_cap]; a sequence of length 0 gets output 0
+ *   scale       softmax scale; 0 or negative means 1 / sqrt(D)
+ *   out         [B, Hq, D], out_dtype FP8SG_BF16 (round to nearest even) or FP8SG_F32
+ *   workspace   at least fp8_kv_decode_attention_workspace_size(...) bytes, 16-byte aligned
+ *   D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}.
+ * The result does not depend on timing: chunk partials are combined in a fixed order.
+ */
+fp8sg_status fp8_kv_decode_attention(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                     const float* k_scales, const float* v_scales, int fmt,
+                                     const int32_t* lengths, int64_t B, int64_t S_cap, int64_t Hq,
+                                     int64_t Hkv, int64_t D, float scale, void* out, int out_dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }
