@@ -14,8 +14,10 @@ Modules:
   kv     -- KV-cache calibrate / quantize / dequantize / append
   blockwise -- 1 x 128 activation groups, 128 x 128 weight blocks, and the
             GEMM that scales each 128-deep partial sum by its own scales
+  attention -- decode attention over an FP8 KV cache with per-head scales
+            (standard softmax; the online recurrence, as a pinned statement)
   native -- the same encoder in plain C (oracle/c/fp8_oracle.c) for sweeps
             over every float32 bit pattern; loaded from its built library
 """
 
-from . import blockwise, fp8, kv, w8a8  # noqa: F401
+from . import attention, blockwise, fp8, kv, w8a8  # noqa: F401

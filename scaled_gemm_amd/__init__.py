@@ -21,6 +21,8 @@ from .fp8sg import (  # noqa: F401
     declared_symbols,
     fp8_kv_append,
     fp8_kv_calibrate,
+    fp8_kv_decode_attention,
+    fp8_kv_decode_attention_workspace_size,
     fp8_kv_dequant,
     fp8_kv_quant,
     fp8_pack_weights,

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -340,6 +340,55 @@ fp8sg_status fp8_kv_append(const uint16_t* kv_new, const int32_t* pos, int64_t B
     if (st != FP8SG_OK) return st;
     return launched(fp8sg::launch_kv_append(kv_new, pos, B, S_cap, H, D, head_scales, fmt == FP8SG_E4M3 ? 0 : 1,
                                             cache, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+bool attn_shape_ok(int64_t B, int64_t S_cap, int64_t Hq, int64_t Hkv, int64_t D) {
+    if (B < 0 || S_cap < 0 || Hq < 0 || Hkv <= 0 || D != 128) return false;
+    if (B >= kMaxDim || S_cap >= kMaxDim || Hq >= 65536 || Hkv >= 65536) return false;
+    if (Hq % Hkv != 0) return false;
+    const int64_t G = Hq / Hkv;
+    if (Hq > 0 && !(G == 1 || G == 2 || G == 4 || G == 8)) return false;
+    const __int128 cache = (__int128)B * S_cap * Hkv * D;
+    const __int128 grid = (__int128)B * Hkv * ((S_cap + 1023) / 1024);
+    return cache < ((__int128)1 << 62) && grid < kMaxDim && (__int128)B * Hq < kMaxDim;
+}
+}  // namespace
+
+extern "C" {
+
+size_t fp8_kv_decode_attention_workspace_size(int64_t B, int64_t S_cap, int64_t Hq, int64_t Hkv, int64_t D) {
+    if (!attn_shape_ok(B, S_cap, Hq, Hkv, D) || B == 0 || Hq == 0) return 0;
+    return fp8sg::attn_workspace_bytes(B, S_cap, Hq, Hkv);
+}
+
+fp8sg_status fp8_kv_decode_attention(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                     const float* k_scales, const float* v_scales, int fmt, const int32_t* lengths,
+                                     int64_t B, int64_t S_cap, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                                     void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    if (!is_fp8(fmt)) return FP8SG_E_DTYPE;
+    if (!(out_dtype == FP8SG_BF16 || out_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
+    if (!attn_shape_ok(B, S_cap, Hq, Hkv, D)) return FP8SG_E_SHAPE;
+    if (!(scale == scale) || scale == __builtin_inff()) return FP8SG_E_SHAPE;  // NaN or +inf softmax scale
+    if (B == 0 || Hq == 0) return FP8SG_OK;
+    if (!q || !k_scales || !v_scales || !lengths || !out) return FP8SG_E_NULL;
+    if (S_cap > 0 && (!k_cache || !v_cache)) return FP8SG_E_NULL;
+    if (!aligned(q, 16) || !aligned(out, 16) || (k_cache && !aligned(k_cache, 16)) ||
+        (v_cache && !aligned(v_cache, 16)) || !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(lengths, 4))
+        return FP8SG_E_ALIGN;
+    const size_t need = fp8_kv_decode_attention_workspace_size(B, S_cap, Hq, Hkv, D);
+    if (!workspace || workspace_bytes < need) return FP8SG_E_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    const float sc = scale > 0.0f ? scale : 1.0f / __builtin_sqrtf((float)D);
+    return launched(fp8sg::launch_kv_decode_attention(q, k_cache, v_cache, k_scales, v_scales,
+                                                      fmt == FP8SG_E4M3 ? 0 : 1, lengths, B, S_cap, Hq, Hkv, sc, out,
+                                                      out_dtype == FP8SG_BF16, (float*)workspace,
+                                                      (hipStream_t)stream));
 }
 
 }  // extern "C"

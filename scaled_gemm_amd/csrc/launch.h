@@ -57,4 +57,11 @@ hipError_t launch_kv_dequant(const uint8_t* kvq, int64_t numel, int64_t H, int64
 hipError_t launch_kv_append(const uint16_t* kv_new, const int32_t* pos, int64_t B, int64_t S_cap, int64_t H,
                             int64_t D, const float* head_scales, int fmt, uint8_t* cache, hipStream_t stream);
 
+// Decode attention over an FP8 KV cache (head dim 128; G = Hq / Hkv in {1, 2, 4, 8}).
+size_t attn_workspace_bytes(int64_t B, int64_t S_cap, int64_t Hq, int64_t Hkv);
+hipError_t launch_kv_decode_attention(const uint16_t* q, const uint8_t* kc, const uint8_t* vc, const float* k_scales,
+                                      const float* v_scales, int fmt, const int32_t* lengths, int64_t B,
+                                      int64_t S_cap, int64_t Hq, int64_t Hkv, float scale, void* out, bool out_bf16,
+                                      float* part, hipStream_t stream);
+
 }  // namespace fp8sg

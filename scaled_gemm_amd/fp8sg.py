@@ -62,6 +62,9 @@ _SIGS = {
     "fp8_quant_per_token_group": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]),
     "fp8_quant_weight_blockwise": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_blockwise": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
+    "fp8_kv_decode_attention_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "fp8_kv_decode_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _i64,
+                                       ctypes.c_float, _vp, _i32, _vp, _sz, _vp]),
     "fp8_kv_calibrate": (_i32, [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp]),
     "fp8_kv_quant": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
     "fp8_kv_dequant": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp]),
@@ -385,3 +388,37 @@ def fp8_kv_append(kv_new: torch.Tensor, pos: torch.Tensor, head_scales: torch.Te
     _check(lib().fp8_kv_append(_ptr(kv_new), _ptr(pos), B, S_cap, H, D, _ptr(head_scales), _FMT[fmt], _ptr(cache),
                                _stream(stream)), "fp8_kv_append")
     return cache
+
+
+def fp8_kv_decode_attention_workspace_size(B: int, S_cap: int, Hq: int, Hkv: int, D: int) -> int:
+    return int(lib().fp8_kv_decode_attention_workspace_size(B, S_cap, Hq, Hkv, D))
+
+
+def fp8_kv_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: torch.Tensor,
+                            v_scales: torch.Tensor, lengths: torch.Tensor, fmt="e4m3", scale: Optional[float] = None,
+                            out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q [B, Hq, D] bf16; caches [B, S_cap, Hkv, D] uint8 codes; per-head scales
+    [Hkv] fp32; lengths [B] int32 -> out [B, Hq, D] (bf16 or fp32)."""
+    _need(q, "q", (torch.bfloat16,))
+    _need(k_cache, "k_cache", (torch.uint8,))
+    B, S_cap, Hkv, D = _kv_dims(k_cache)
+    _need(v_cache, "v_cache", (torch.uint8,), (B, S_cap, Hkv, D))
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected (B, Hq, D) = ({B}, Hq, {D})")
+    Hq = int(q.shape[1])
+    _need(k_scales, "k_scales", (torch.float32,), (Hkv,))
+    _need(v_scales, "v_scales", (torch.float32,), (Hkv,))
+    _need(lengths, "lengths", (torch.int32,), (B,))
+    o_code = {torch.bfloat16: BF16, torch.float32: F32}[out_dtype]
+    out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device) if out is None else out
+    _need(out, "out", (out_dtype,), (B, Hq, D))
+    need = fp8_kv_decode_attention_workspace_size(B, S_cap, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().fp8_kv_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+                                         _FMT[fmt], _ptr(lengths), B, S_cap, Hq, Hkv, D,
+                                         0.0 if scale is None else float(scale), _ptr(out), o_code, _ptr(workspace),
+                                         ws_bytes, _stream(stream)), "fp8_kv_decode_attention")
+    return out

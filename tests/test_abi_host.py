@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     names = sg.declared_symbols()
-    assert len(names) == 17
+    assert len(names) == 19
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
     missing = [n for n in names if n not in exported]
@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert sg.lib().fp8sg_version() == 5
+    assert sg.lib().fp8sg_version() == 6
     for st in range(8):
         assert sg.status_string(st)
     assert sg.status_string(99) == "unknown status"
@@ -71,6 +71,34 @@ def test_blockwise_validation(lib):
     assert g(A, None, A, 0, A, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_NULL
     assert g(A, A, A, 0, A + 2, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_ALIGN
     assert g(None, None, None, 0, None, None, b.BF16, 0, 8, 128, b.ACCUM_MFMA_FP8, None) == b.OK
+
+
+def test_attention_validation(lib):
+    f = lib.fp8_kv_decode_attention
+    ws = lib.fp8_kv_decode_attention_workspace_size(8, 32768, 32, 8, 128)
+    assert ws == 8 * 8 * 32 * 4 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 32768, 32, 8, 64) == 0   # D must be 128
+
+    def call(**kw):
+        d = dict(q=A, k=A, v=A, sk=A, sv=A, fmt=b.E4M3, L=A, B=8, S=32768, Hq=32, Hkv=8, D=128, scale=0.0, out=A,
+                 odt=b.BF16, ws=A, wsb=ws)
+        d.update(kw)
+        return f(d["q"], d["k"], d["v"], d["sk"], d["sv"], d["fmt"], d["L"], d["B"], d["S"], d["Hq"], d["Hkv"],
+                 d["D"], d["scale"], d["out"], d["odt"], d["ws"], d["wsb"], None)
+
+    assert call(fmt=b.BF16) == b.E_DTYPE
+    assert call(odt=b.E4M3) == b.E_DTYPE
+    assert call(D=64) == b.E_SHAPE
+    assert call(Hq=30) == b.E_SHAPE           # not a multiple of Hkv
+    assert call(Hq=24) == b.E_SHAPE           # G = 3
+    assert call(Hq=128) == b.E_SHAPE          # G = 16
+    assert call(scale=float("nan")) == b.E_SHAPE
+    assert call(L=None) == b.E_NULL
+    assert call(v=None) == b.E_NULL
+    assert call(q=A + 8) == b.E_ALIGN
+    assert call(wsb=ws - 1) == b.E_WORKSPACE
+    assert call(ws=None) == b.E_WORKSPACE
+    assert call(B=0, q=None, k=None, v=None, out=None) == b.OK
 
 
 def test_quant_validation(lib):

@@ -34,6 +34,7 @@ __all__ = [
     "large_layer_inputs",
     "kv_inputs",
     "kv_append_inputs",
+    "attention_queries",
     "STATIC_SCALE_NUM",
     "STATIC_SCALE_DEN",
 ]
@@ -150,3 +151,10 @@ def kv_append_inputs(k_channels, v_channels, seed: int = 0, b: int = 8, h: int =
         x[:, ch] *= np.float32(20.0)
         out.append(bf16_bits_from_f32(x).reshape(b, h, d))
     return out[0], out[1]
+
+
+def attention_queries(seed: int = 0, b: int = 8, hq: int = 32, d: int = 128):
+    """Decode-attention queries: q bf16 [b, hq, d] ~ N(0, 1), one new token per
+    sequence and query head (hq = 32 query heads over the 8 kv heads of the
+    KV-cache case: groups of 4, the Llama-3-8B-class geometry)."""
+    return bf16_bits_from_f32(normal_f32(_rng(seed, 6, 0), (b, hq * d)).reshape(b, hq, d))
