@@ -65,7 +65,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--quick", action="store_true", help="headline only: skip the detail workloads")
     ap.add_argument("--workload", nargs="*", default=None,
-                    help="detail workloads to run (default all): prefill large quant kv weights blockwise fp8out")
+                    help="detail workloads to run (default all): prefill large quant kv weights blockwise fp8out "
+                         "attention")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -200,7 +201,7 @@ def main():
 
     # ------------------------------------------------------------ details
     wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights", "blockwise",
-                                                       "fp8out"}
+                                                       "fp8out", "attention"}
     if args.quick:
         wanted = set()
     del wqs[1:], wrm[1:]
@@ -475,7 +476,7 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
         del aq, ap, wq, wp, yq
         torch.cuda.empty_cache()
 
-    if "kv" in wanted:
+    if "kv" in wanted or "attention" in wanted:
         log("kv cache")
         k, v, kc, vc = kv_inputs(0)
         B, S, H, D = k.shape
@@ -501,6 +502,27 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
             out.append({"workload": f"KV dequant K+V [{B},{S},{H},{D}] {fmt}", "avg_us": round(float(d.mean()) * 1e3, 1),
                         "GB_s": _gbs(6 * numel, d.mean()), "frac_hbm": round(_gbs(6 * numel, d.mean()) / HBM_PEAK_GBS, 4)})
             del qk, qv, dk, dv
+        if "attention" in wanted:
+            # one decode step of attention over the quantized cache: 32 query heads over the 8 kv heads
+            from workloads import attention_queries
+            qt = to_bf16(attention_queries(0, b=B, hq=32, d=D))
+            Lt = torch.full((B,), S, dtype=torch.int32, device=dev)
+            ao = torch.empty((B, 32, D), dtype=torch.bfloat16, device=dev)
+            aws = torch.empty(sg.fp8_kv_decode_attention_workspace_size(B, S, 32, H, D), dtype=torch.uint8,
+                              device=dev)
+            for fmt in ("e4m3", "e5m2"):
+                sk = sg.fp8_kv_calibrate(kt, fmt)
+                sv = sg.fp8_kv_calibrate(vt, fmt)
+                qk = sg.fp8_kv_quant(kt, sk, fmt)
+                qv = sg.fp8_kv_quant(vt, sv, fmt)
+                d = timed_events(lambda i: sg.fp8_kv_decode_attention(qt, qk, qv, sk, sv, Lt, fmt, out=ao,
+                                                                      workspace=aws), 20, 3, reps=3)
+                nbytes = 2 * numel + 2 * 2 * B * 32 * D + 8 * H
+                out.append({"workload": f"KV decode attention q [{B},32,{D}] over K+V [{B},{S},{H},{D}] {fmt}",
+                            "avg_us": round(float(d.mean()) * 1e3, 1), "GB_s": _gbs(nbytes, d.mean()),
+                            "frac_hbm": round(_gbs(nbytes, d.mean()) / HBM_PEAK_GBS, 4)})
+                del qk, qv
+            torch.cuda.empty_cache()
         kn, vn = kv_append_inputs(kc, vc)
         knt, vnt = to_bf16(kn), to_bf16(vn)
         del kt, vt

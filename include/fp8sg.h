@@ -343,7 +343,7 @@ size_t fp8_kv_decode_attention_workspace_size(int64_t B, int64_t S_cap, int64_t 
  *   scale       softmax scale; 0 or negative means 1 / sqrt(D)
  *   out         [B, Hq, D], out_dtype FP8SG_BF16 (round to nearest even) or FP8SG_F32
  *   workspace   at least fp8_kv_decode_attention_workspace_size(...) bytes, 16-byte aligned
- *   D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}.
+ *   D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}; S_cap <= 2^20.
  * The result does not depend on timing: chunk partials are combined in a fixed order.
  */
 fp8sg_status fp8_kv_decode_attention(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,

@@ -347,7 +347,7 @@ fp8sg_status fp8_kv_append(const uint16_t* kv_new, const int32_t* pos, int64_t B
 namespace {
 bool attn_shape_ok(int64_t B, int64_t S_cap, int64_t Hq, int64_t Hkv, int64_t D) {
     if (B < 0 || S_cap < 0 || Hq < 0 || Hkv <= 0 || D != 128) return false;
-    if (B >= kMaxDim || S_cap >= kMaxDim || Hq >= 65536 || Hkv >= 65536) return false;
+    if (B >= kMaxDim || S_cap > ((int64_t)1 << 20) || Hq >= 65536 || Hkv >= 65536) return false;  // chunk weights in LDS
     if (Hq % Hkv != 0) return false;
     const int64_t G = Hq / Hkv;
     if (Hq > 0 && !(G == 1 || G == 2 || G == 4 || G == 8)) return false;

@@ -139,9 +139,11 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
         for (int d = 0; d < 16; ++d) o[h][d] = 0.0f;
     float m_run = -__builtin_inff(), l_run = 0.0f;  // for head jh (lanes with jh < kG)
 
-    for (int t0 = t_begin + wave * kBlk; t0 < t_end; t0 += 4 * kBlk) {
-        // ---- loads: K slices for the 4 score tiles, V slices for the 8 p.V steps
-        uint4 kr[4][2], vr[8];
+    // K slices for the 4 score tiles and V slices for the 8 p.V steps of the
+    // block at t0 (positions past t_end clamped to the last valid one; their
+    // scores are masked).  The next block's loads are issued before the
+    // current block is computed.
+    auto load_block = [&](uint4 (&kr)[4][2], uint4 (&vr)[8], int t0) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             int t = t0 + 16 * i + jh;
@@ -156,6 +158,12 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
             t = t < t_end ? t : t_end - 1;
             vr[k] = *reinterpret_cast<const uint4*>(vb + (int64_t)t * row_stride + 16 * dg);
         }
+    };
+    uint4 kr[4][2], vr[8];
+    if (t_begin + wave * kBlk < t_end) load_block(kr, vr, t_begin + wave * kBlk);
+    for (int t0 = t_begin + wave * kBlk; t0 < t_end; t0 += 4 * kBlk) {
+        uint4 kn[4][2], vn[8];
+        if (t0 + 4 * kBlk < t_end) load_block(kn, vn, t0 + 4 * kBlk);
         // ---- scores: 4 tiles of 16 positions x 16 head columns
         float x[4][4];
 #pragma unroll
@@ -220,6 +228,13 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
             }
         }
         __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kr[i][0] = kn[i][0];
+            kr[i][1] = kn[i][1];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vr[k] = vn[k];
     }
 
     // ---- combine the 8 position slots of each dim group (xor over lane bits 3..5)
@@ -266,11 +281,18 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
     }
 }
 
-// Workgroup (b, h), one thread per dimension: the chunks' partials in chunk order.
+// Workgroup (b, h), one thread per dimension: the chunks' partials in chunk
+// order.  The chunk maxima and sums are first read by all threads at once (one
+// chunk per thread) and their weights exp(m_c - M) kept in LDS; then each
+// thread adds its dimension of the chunks' outputs, 8 chunks per batch of loads.
+constexpr int kMaxChunks = 1024;  // S_cap <= 2^20
+
 template <bool kOutBf16>
 __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ part, const float* __restrict__ v_scales,
                                                     const int32_t* __restrict__ lengths, int S_cap, int Hkv, int G,
                                                     int nchunk, void* __restrict__ out) {
+    __shared__ float wgt[kMaxChunks];
+    __shared__ float red[2];
     const int h = (int)(blockIdx.x % (unsigned)(Hkv * G));
     const int b = (int)(blockIdx.x / (unsigned)(Hkv * G));
     const int g = h / G, j = h % G;
@@ -278,16 +300,45 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
     int L = lengths[b];
     L = L < 0 ? 0 : (L > S_cap ? S_cap : L);
     const int nc = (L + kChunk - 1) / kChunk;
-    const float* pb = part + ((size_t)(b * Hkv + g) * nchunk) * G * kPartFloats + (size_t)j * kPartFloats;
-    float M = -__builtin_inff();
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, pb[(size_t)c * G * kPartFloats + kAttnD]);
-    float acc = 0.0f, lsum = 0.0f;
-    for (int c = 0; c < nc; ++c) {
-        const float* pc = pb + (size_t)c * G * kPartFloats;
-        const float f = __expf(pc[kAttnD] - M);
-        acc += f * pc[d];
-        lsum += f * pc[kAttnD + 1];
+    const size_t stride = (size_t)G * kPartFloats;
+    const float* pb = part + ((size_t)(b * Hkv + g) * nchunk) * stride + (size_t)j * kPartFloats;
+    // chunk maxima -> M (every chunk c < nc holds at least one position, so its m is finite)
+    float mx = -__builtin_inff();
+    for (int c = d; c < nc; c += blockDim.x) {
+        const float m = pb[(size_t)c * stride + kAttnD];
+        wgt[c] = m;
+        mx = fmaxf(mx, m);
     }
+    mx = wave_max(mx);
+    if ((d & 63) == 0) red[d >> 6] = mx;
+    __syncthreads();
+    const float M = fmaxf(red[0], red[1]);
+    __syncthreads();
+    float ls = 0.0f;
+    for (int c = d; c < nc; c += blockDim.x) {
+        const float f = __expf(wgt[c] - M);
+        wgt[c] = f;
+        ls += f * pb[(size_t)c * stride + kAttnD + 1];
+    }
+    ls = ls + __shfl_xor(ls, 32, 64);
+    ls = ls + __shfl_xor(ls, 16, 64);
+    ls = ls + __shfl_xor(ls, 8, 64);
+    ls = ls + __shfl_xor(ls, 4, 64);
+    ls = ls + __shfl_xor(ls, 2, 64);
+    ls = ls + __shfl_xor(ls, 1, 64);
+    if ((d & 63) == 0) red[d >> 6] = ls;
+    __syncthreads();
+    const float lsum = red[0] + red[1];
+    float acc = 0.0f;
+    int c = 0;
+    for (; c + 8 <= nc; c += 8) {
+        float ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ov[u] = pb[(size_t)(c + u) * stride + d];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += wgt[c + u] * ov[u];
+    }
+    for (; c < nc; ++c) acc += wgt[c] * pb[(size_t)c * stride + d];
     const float r = nc > 0 ? (acc / lsum) * v_scales[g] : 0.0f;
     const size_t o_idx = ((size_t)b * Hkv * G + h) * kAttnD + d;
     if (kOutBf16) ((uint16_t*)out)[o_idx] = (uint16_t)(pack_bf16x2(r, 0.0f) & 0xFFFFu);
