@@ -97,7 +97,10 @@ typedef enum fp8sg_layout {
      * fp8_pack_weights applied to [M, K] codes: ceil(M / 16) * 16 * K bytes.
      * Activations that fp8_scaled_gemm quantizes itself go to its workspace
      * in this order when M <= 32. */
-    FP8SG_A_PACKED = 2
+    FP8SG_A_PACKED = 2,
+    /* fp8_quant_mx only: the E8M0 scales in the packed layout that
+     * fp8_scaled_gemm_mx reads (see fp8_pack_mx_scales). */
+    FP8SG_MX_SCALES_PACKED = 4
 } fp8sg_layout;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -276,6 +279,81 @@ fp8sg_status fp8_quant_weight_blockwise(const void* w, int w_dtype, int64_t N, i
 fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales, const uint8_t* wq, int layout,
                                        const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N,
                                        int64_t K, int accum, void* stream);
+
+/*
+ * MXFP8 (microscaling): every 32 consecutive k of a row share one power-of-two
+ * scale, stored as an E8M0 byte e with the value 2^(e - 127) (e = 255, NaN, is
+ * never written).  Small blocks with an 8-bit scale each ("Quantization for LLM
+ * inference: FP8, INT4 (GPTQ, AWQ) and GGUF", blog.lo0.es -- "Microscaling:
+ * NVFP4 and MXFP4"), contiguous along the reduction dimension ("Quantization:
+ * FP8 inference and KV-cache quantization" -- "Training in FP8 or lower").
+ * The scale of a block is the smallest 2^k with amax <= FMAX * 2^k (the
+ * dynamic rule s = amax / FMAX rounded up to a power of two, so no element
+ * saturates), k clamped to [-127, 127], and 2^0 for a block of zeros; a value
+ * is encoded as FMT(RN32(x / 2^k)) with the library's rounding rule.
+ *
+ * MX fragment order of packed codes: the 2048-byte block of (16-row tile t,
+ * 128-k block kb) sits at (t * K/128 + kb) * 2048, as for FP8SG_W_PACKED, but
+ * lane l's first 16 bytes (at 16 l) are k 128 kb + 16 (l / 16) + [0, 16) of
+ * row 16 t + l % 16 and its second 16 bytes (at 1024 + 16 l) are
+ * k 128 kb + 64 + 16 (l / 16) + [0, 16): the k order of gfx950's scaled matrix
+ * cores, which apply scale l / 16 of the block to k [32 (l / 16), +32).  Codes
+ * packed by fp8_pack_weights are NOT in this order.
+ *
+ * Packed scale layout (what fp8_scaled_gemm_mx reads): for 128-deep k block
+ * kb and group g of four 16-row tiles, 256 bytes at (kb * T4 + g) * 256 with
+ * T4 = ceil(rows / 64); inside, byte 4 l + j is the scale of row
+ * 16 (4 g + j) + l % 16 for the 32-k group l / 16 of block kb (l = 0..63,
+ * j = 0..3).  Rows past `rows` hold 127 when written by fp8_pack_mx_scales and
+ * are left unwritten by fp8_quant_mx.
+ */
+
+/* Bytes of a packed MX scale buffer for [rows, K] codes: ceil(rows / 64) * 256
+ * * (K / 128).  Host-only; no HIP call. */
+size_t fp8_mx_packed_scale_bytes(int64_t rows, int64_t K);
+
+/*
+ * MXFP8 quantization of the rows of x (activations or, offline, weights).
+ *   x       [rows, K] FP8SG_BF16 or FP8SG_F32
+ *   fmt     element format: FP8SG_E4M3 (FMAX 448) or FP8SG_E5M2 (FMAX 57344)
+ *   q       codes (output): [rows, K] row-major, or with FP8SG_A_PACKED in
+ *           layout the MX fragment order above (fp8_packed_weight_bytes(rows, K)
+ *           bytes; padding rows unwritten) -- for weights, quantize straight
+ *           into this order offline
+ *   scales  E8M0 bytes (output): [rows, K / 32] row-major, or with
+ *           FP8SG_MX_SCALES_PACKED the packed layout above
+ *           (fp8_mx_packed_scale_bytes(rows, K) bytes)
+ *   layout  0 or an OR of FP8SG_A_PACKED and FP8SG_MX_SCALES_PACKED
+ *   K % 32 == 0 (K % 128 == 0 with either packed flag).
+ */
+fp8sg_status fp8_quant_mx(const void* x, int x_dtype, int64_t rows, int64_t K, int fmt, uint8_t* q,
+                          uint8_t* scales, int layout, void* stream);
+
+/*
+ * Row-major E8M0 scales [rows, K / 32] -> the packed layout above (for
+ * weights: once, offline).  packed holds fp8_mx_packed_scale_bytes(rows, K)
+ * bytes; K % 128 == 0.
+ */
+fp8sg_status fp8_pack_mx_scales(const uint8_t* scales, int64_t rows, int64_t K, uint8_t* packed, void* stream);
+
+/*
+ * MXFP8 GEMM on the gfx950 scaled matrix cores: each 32-deep partial product
+ * is scaled by its two block scales and the results accumulate in fp32:
+ *   y[m, n] = sum_b 2^(ka[m, b] + kw[n, b]) sum_{k = 32 b}^{32 b + 31} a[m, k] w[n, k].
+ * The matrix cores sum each group of 8 consecutive products with the in-
+ * instruction alignment described at fp8sg_accum (FP8SG_ACCUM_MFMA_FP8).
+ *   a_q       [M, K] codes of format a_fmt (FP8SG_E4M3 or FP8SG_E5M2),
+ *             row-major, or with FP8SG_A_PACKED the MX fragment order
+ *   a_scales  packed E8M0 scales of a (fp8_mx_packed_scale_bytes(M, K) bytes)
+ *   wq        [N, K] E4M3 codes, row-major, or with FP8SG_W_PACKED the MX fragment order
+ *   w_scales  packed E8M0 scales of W (fp8_mx_packed_scale_bytes(N, K) bytes)
+ *   y         [M, N] FP8SG_BF16 (round to nearest even) or FP8SG_F32
+ *   layout    0 or an OR of FP8SG_W_PACKED and FP8SG_A_PACKED
+ *   K % 128 == 0; M, N >= 0 arbitrary.
+ */
+fp8sg_status fp8_scaled_gemm_mx(const uint8_t* a_q, const uint8_t* a_scales, int a_fmt, const uint8_t* wq,
+                                const uint8_t* w_scales, int layout, void* y, int y_dtype, int64_t M, int64_t N,
+                                int64_t K, void* stream);
 
 /*
  * KV-cache calibration: one scale per kv head, s_h = RN32(amax_h / max) over

@@ -16,6 +16,7 @@ from .fp8sg import (  # noqa: F401
     SCALE_PER_TENSOR,
     SCALE_PER_TOKEN,
     A_PACKED,
+    MX_SCALES_PACKED,
     W_PACKED,
     W_ROW_MAJOR,
     declared_symbols,
@@ -25,8 +26,11 @@ from .fp8sg import (  # noqa: F401
     fp8_kv_decode_attention_workspace_size,
     fp8_kv_dequant,
     fp8_kv_quant,
+    fp8_mx_packed_scale_bytes,
+    fp8_pack_mx_scales,
     fp8_pack_weights,
     fp8_packed_weight_bytes,
+    fp8_quant_mx,
     fp8_quant_per_tensor_static,
     fp8_quant_per_token_group,
     fp8_quant_weight_blockwise,
@@ -35,6 +39,7 @@ from .fp8sg import (  # noqa: F401
     fp8_scaled_gemm,
     fp8_scaled_gemm_blockwise,
     fp8_scaled_gemm_fp8out,
+    fp8_scaled_gemm_mx,
     fp8_scaled_gemm_workspace_size,
     lib,
     status_string,

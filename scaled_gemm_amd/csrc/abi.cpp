@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -282,6 +282,59 @@ fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales
     return launched(fp8sg::launch_gemm_blockwise(a_q, (layout & FP8SG_A_PACKED) != 0, a_scales, wq,
                                                  (layout & FP8SG_W_PACKED) != 0, w_scales, y, y_dtype == FP8SG_BF16,
                                                  M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, (hipStream_t)stream));
+}
+
+size_t fp8_mx_packed_scale_bytes(int64_t rows, int64_t K) {
+    if (rows <= 0 || K <= 0) return 0;
+    return (size_t)((rows + 63) / 64) * 256 * (size_t)(K / 128);
+}
+
+fp8sg_status fp8_quant_mx(const void* x, int x_dtype, int64_t rows, int64_t K, int fmt, uint8_t* q,
+                          uint8_t* scales, int layout, void* stream) {
+    if (!is_hp(x_dtype) || !is_fp8(fmt)) return FP8SG_E_DTYPE;
+    if ((layout & ~(FP8SG_A_PACKED | FP8SG_MX_SCALES_PACKED)) != 0) return FP8SG_E_DTYPE;
+    if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (K % (layout != 0 ? 128 : 32) != 0) return FP8SG_E_SHAPE;
+    if (rows * (K / 8) >= kMaxDim * 256) return FP8SG_E_SHAPE;  // one thread per 8 elements
+    if (rows == 0 || K == 0) return FP8SG_OK;
+    if (!x || !q || !scales) return FP8SG_E_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    return launched(fp8sg::launch_mx_quant(x, x_dtype == FP8SG_BF16, rows, K, fmt == FP8SG_E4M3 ? 0 : 1, q,
+                                           (layout & FP8SG_A_PACKED) != 0, scales,
+                                           (layout & FP8SG_MX_SCALES_PACKED) != 0, (hipStream_t)stream));
+}
+
+fp8sg_status fp8_pack_mx_scales(const uint8_t* scales, int64_t rows, int64_t K, uint8_t* packed, void* stream) {
+    if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim || K % 128 != 0) return FP8SG_E_SHAPE;
+    if (rows == 0 || K == 0) return FP8SG_OK;
+    if (fp8_mx_packed_scale_bytes(rows, K) / 256 >= (size_t)kMaxDim) return FP8SG_E_SHAPE;
+    if (!scales || !packed) return FP8SG_E_NULL;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    return launched(fp8sg::launch_pack_mx_scales(scales, rows, K, packed, (hipStream_t)stream));
+}
+
+fp8sg_status fp8_scaled_gemm_mx(const uint8_t* a_q, const uint8_t* a_scales, int a_fmt, const uint8_t* wq,
+                                const uint8_t* w_scales, int layout, void* y, int y_dtype, int64_t M, int64_t N,
+                                int64_t K, void* stream) {
+    if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32) || !is_fp8(a_fmt)) return FP8SG_E_DTYPE;
+    if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED)) != 0) return FP8SG_E_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (K % 128 != 0) return FP8SG_E_SHAPE;
+    if (M == 0 || N == 0) return FP8SG_OK;
+    if (!y) return FP8SG_E_NULL;
+    if (K > 0 && (!a_q || !wq || !a_scales || !w_scales)) return FP8SG_E_NULL;
+    if ((a_q && !aligned(a_q, 16)) || (wq && !aligned(wq, 16)) || !aligned(y, 16)) return FP8SG_E_ALIGN;
+    if ((a_scales && !aligned(a_scales, 4)) || (w_scales && !aligned(w_scales, 4))) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    // K == 0 launches too: the kernels read no operand and write the empty sums (zeros)
+    return launched(fp8sg::launch_gemm_mx(a_q, (layout & FP8SG_A_PACKED) != 0, a_scales, a_fmt == FP8SG_E4M3 ? 0 : 1,
+                                          wq, (layout & FP8SG_W_PACKED) != 0, w_scales, y,
+                                          y_dtype == FP8SG_BF16 ? fp8sg::kOutBF16 : fp8sg::kOutF32, M, N, K,
+                                          (hipStream_t)stream));
 }
 
 fp8sg_status fp8_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,

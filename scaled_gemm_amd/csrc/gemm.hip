@@ -572,16 +572,6 @@ constexpr int kBwOps = 32 * kPackBlock;       // A 32 KB + W 32 KB
 constexpr int kBwStage = kBwOps + 2048;       // + s_a (256 floats) + s_w (4 x 64 floats)
 constexpr int kBwCopies = 9;                  // copies per wave per stage
 
-__device__ __forceinline__ void copy4_to_lds(const float* src, uint32_t lds_addr) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dword %1, off"
-        :
-        : "s"(lds_addr), "v"(src)
-        : "memory", "m0");
-}
-
 template <int kOut, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __restrict__ A,
                                                              const float* __restrict__ sa,

@@ -200,6 +200,17 @@ __device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint32_t lds_a
         : "memory", "m0");
 }
 
+// The four-byte form (global_load_lds_dword): lane l's 4 bytes land at M0 + 4 l.
+__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off"
+        :
+        : "s"(lds_addr), "v"(src)
+        : "memory", "m0");
+}
+
 __device__ __forceinline__ void issue_tile_copy(uint8_t* __restrict__ lds, const uint8_t* __restrict__ tile,
                                                 int64_t kb_off, int wave, const uint32_t (&o)[8]) {
     const uint8_t* base = tile + kb_off;

@@ -46,6 +46,18 @@ hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* 
                                  bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N,
                                  int64_t K, bool fp8_mfma, hipStream_t stream);
 
+// MXFP8: E8M0 scale bytes per 32 consecutive k (fmt 0 = E4M3, 1 = E5M2).  Scales
+// row-major [R, K / 32] or in the GEMM's packed layout; codes row-major or in
+// the fragment order; K % 32 == 0 (K % 128 == 0 for either packed form).
+hipError_t launch_mx_quant(const void* x, bool x_is_bf16, int64_t R, int64_t K, int fmt, uint8_t* q,
+                           bool packed_codes, uint8_t* scales, bool packed_scales, hipStream_t stream);
+hipError_t launch_pack_mx_scales(const uint8_t* s, int64_t R, int64_t K, uint8_t* p, hipStream_t stream);
+// MXFP8 GEMM: W E4M3, A E4M3 (a_fmt 0) or E5M2 (1), both scale arrays packed;
+// out_kind kOutF32 or kOutBF16.
+hipError_t launch_gemm_mx(const uint8_t* aq, bool a_packed, const uint8_t* a_scales, int a_fmt, const uint8_t* wq,
+                          bool w_packed, const uint8_t* w_scales, void* y, int out_kind, int64_t M, int64_t N,
+                          int64_t K, hipStream_t stream);
+
 hipError_t launch_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, hipStream_t stream);
 
 hipError_t launch_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,

@@ -26,7 +26,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8sg.h")
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_DEVICE, E_LAUNCH, E_WORKSPACE = range(8)
 F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
 SCALE_PER_TOKEN, SCALE_PER_TENSOR = 0, 1
-W_ROW_MAJOR, W_PACKED, A_PACKED = 0, 1, 2
+W_ROW_MAJOR, W_PACKED, A_PACKED, MX_SCALES_PACKED = 0, 1, 2, 4
 ACCUM_EXACT, ACCUM_MFMA_FP8 = 0, 1
 
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
@@ -62,6 +62,10 @@ _SIGS = {
     "fp8_quant_per_token_group": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]),
     "fp8_quant_weight_blockwise": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_blockwise": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
+    "fp8_mx_packed_scale_bytes": (_sz, [_i64, _i64]),
+    "fp8_quant_mx": (_i32, [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _i32, _vp]),
+    "fp8_pack_mx_scales": (_i32, [_vp, _i64, _i64, _vp, _vp]),
+    "fp8_scaled_gemm_mx": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp]),
     "fp8_kv_decode_attention_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "fp8_kv_decode_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _i64,
                                        ctypes.c_float, _vp, _i32, _vp, _sz, _vp]),
@@ -328,6 +332,79 @@ def fp8_scaled_gemm_blockwise(a: torch.Tensor, a_scales: torch.Tensor, wq: torch
     layout = (W_PACKED if w_packed else 0) | (A_PACKED if a_packed else 0)
     _check(lib().fp8_scaled_gemm_blockwise(_ptr(a), _ptr(a_scales), _ptr(wq), layout, _ptr(w_scales), _ptr(y), y_code,
                                            M, N, K, _ACCUM[accum], _stream(stream)), "fp8_scaled_gemm_blockwise")
+    return y
+
+
+def fp8_mx_packed_scale_bytes(rows: int, K: int) -> int:
+    return int(lib().fp8_mx_packed_scale_bytes(rows, K))
+
+
+def fp8_quant_mx(x: torch.Tensor, fmt="e4m3", layout="row_major", scale_layout="row_major",
+                 q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None, stream=None):
+    """x [rows, K] (bf16/fp32) -> (codes, E8M0 scale bytes): one power-of-two
+    scale per 32 consecutive k.  layout="packed": codes in the MX fragment
+    order (1-D, fp8_packed_weight_bytes(rows, K) bytes); scale_layout="packed": the
+    scales in the layout fp8_scaled_gemm_mx reads (1-D,
+    fp8_mx_packed_scale_bytes(rows, K) bytes), else [rows, K / 32]."""
+    _need(x, "x", _HP)
+    R, K = x.shape
+    pc = _LAYOUT[layout] == W_PACKED
+    ps = _LAYOUT[scale_layout] == W_PACKED
+    qshape = (fp8_packed_weight_bytes(R, K),) if pc else (R, K)
+    sshape = (fp8_mx_packed_scale_bytes(R, K),) if ps else (R, K // 32)
+    q = torch.empty(qshape, dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty(sshape, dtype=torch.uint8, device=x.device) if scales is None else scales
+    _need(q, "q", (torch.uint8,), qshape)
+    _need(scales, "scales", (torch.uint8,), sshape)
+    flags = (A_PACKED if pc else 0) | (MX_SCALES_PACKED if ps else 0)
+    _check(lib().fp8_quant_mx(_ptr(x), _hp_code(x), R, K, _FMT[fmt], _ptr(q), _ptr(scales), flags, _stream(stream)),
+           "fp8_quant_mx")
+    return q, scales
+
+
+def fp8_pack_mx_scales(scales: torch.Tensor, packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Row-major E8M0 scales [rows, K / 32] -> the packed layout (1-D)."""
+    _need(scales, "scales", (torch.uint8,))
+    R, nb = scales.shape
+    K = 32 * nb
+    n = fp8_mx_packed_scale_bytes(R, K)
+    packed = torch.empty((n,), dtype=torch.uint8, device=scales.device) if packed is None else packed
+    _need(packed, "packed", (torch.uint8,), (n,))
+    _check(lib().fp8_pack_mx_scales(_ptr(scales), R, K, _ptr(packed), _stream(stream)), "fp8_pack_mx_scales")
+    return packed
+
+
+def fp8_scaled_gemm_mx(a: torch.Tensor, a_scales: torch.Tensor, wq: torch.Tensor, w_scales: torch.Tensor, *,
+                       a_fmt="e4m3", out_dtype=torch.bfloat16, w_layout="row_major", a_layout="row_major",
+                       a_shape: Optional[tuple] = None, w_shape: Optional[tuple] = None,
+                       y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y [M, N] = sum_b 2^(ka + kw) (A_q W_q^T)_b over the 32-deep blocks b.
+
+    a: codes [M, K] of format a_fmt (or the MX-packed 1-D buffer of
+    fp8_quant_mx with a_shape=(M, K)); wq: E4M3 [N, K] (or MX-packed with
+    w_shape=(N, K));
+    a_scales / w_scales: packed E8M0 scales (fp8_quant_mx with
+    scale_layout="packed", or fp8_pack_mx_scales)."""
+    _need(a, "a", (torch.uint8,))
+    _need(wq, "wq", (torch.uint8,))
+    a_packed = _LAYOUT[a_layout] == W_PACKED
+    w_packed = _LAYOUT[w_layout] == W_PACKED
+    M, K = (int(v) for v in a_shape) if a_packed else a.shape
+    N = int(w_shape[0]) if w_packed else wq.shape[0]
+    if a_packed and a.numel() != fp8_packed_weight_bytes(M, K):
+        raise ValueError(f"packed a has {a.numel()} bytes, expected {fp8_packed_weight_bytes(M, K)}")
+    if w_packed and (w_shape is None or int(w_shape[1]) != K or wq.numel() != fp8_packed_weight_bytes(N, K)):
+        raise ValueError("w_layout='packed' takes w_shape=(N, K) and fp8_packed_weight_bytes(N, K) bytes")
+    if not w_packed and wq.shape[1] != K:
+        raise ValueError(f"wq has shape {tuple(wq.shape)}, expected K = {K}")
+    _need(a_scales, "a_scales", (torch.uint8,), (fp8_mx_packed_scale_bytes(M, K),))
+    _need(w_scales, "w_scales", (torch.uint8,), (fp8_mx_packed_scale_bytes(N, K),))
+    y_code = {torch.bfloat16: BF16, torch.float32: F32}[out_dtype]
+    y = torch.empty((M, N), dtype=out_dtype, device=a.device) if y is None else y
+    _need(y, "y", (out_dtype,), (M, N))
+    layout = (W_PACKED if w_packed else 0) | (A_PACKED if a_packed else 0)
+    _check(lib().fp8_scaled_gemm_mx(_ptr(a), _ptr(a_scales), _FMT[a_fmt], _ptr(wq), _ptr(w_scales), layout, _ptr(y),
+                                    y_code, M, N, K, _stream(stream)), "fp8_scaled_gemm_mx")
     return y
 
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     names = sg.declared_symbols()
-    assert len(names) == 19
+    assert len(names) == 23
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
     missing = [n for n in names if n not in exported]
@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert sg.lib().fp8sg_version() == 6
+    assert sg.lib().fp8sg_version() == 7
     for st in range(8):
         assert sg.status_string(st)
     assert sg.status_string(99) == "unknown status"
@@ -230,3 +230,97 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         sg.fp8_quant_per_token(torch.zeros((2, 16), dtype=torch.bfloat16))
+
+
+def pack_mx_scales_reference(s):
+    """The packed MX scale layout written out from its definition in include/fp8sg.h:
+    s [rows, K / 32] E8M0 bytes -> ceil(rows / 64) * 256 * (K / 128) bytes, rows past
+    the end 127."""
+    import numpy as np
+    R, nb = s.shape
+    K = 32 * nb
+    T4 = (R + 63) // 64
+    out = np.zeros((K // 128) * T4 * 256, np.uint8)
+    for kb in range(K // 128):
+        for g in range(T4):
+            for lane in range(64):
+                for j in range(4):
+                    r = 16 * (4 * g + j) + lane % 16
+                    b = 4 * kb + lane // 16
+                    out[(kb * T4 + g) * 256 + 4 * lane + j] = s[r, b] if r < R else 127
+    return out
+
+
+def test_mx_packed_scale_bytes_and_reference_layout():
+    import numpy as np
+    assert sg.fp8_mx_packed_scale_bytes(1, 128) == 256
+    assert sg.fp8_mx_packed_scale_bytes(64, 4096) == 256 * 32
+    assert sg.fp8_mx_packed_scale_bytes(65, 256) == 2 * 256 * 2
+    assert sg.fp8_mx_packed_scale_bytes(0, 128) == 0
+    # the reference is a bijection of the real rows' bytes onto their slots, padding 127
+    rng = np.random.default_rng(0)
+    s = rng.integers(0, 255, (70, 8), dtype=np.uint8)
+    p = pack_mx_scales_reference(s)
+    assert p.size == sg.fp8_mx_packed_scale_bytes(70, 256)
+    assert np.array_equal(np.sort(p[p != 127]), np.sort(s[s != 127].ravel()))
+    assert (p == 127).sum() == (s == 127).sum() + (128 - 70) * 8
+
+
+def test_mx_validation(lib):
+    # quantizer: dtype, format, layout bits, K multiple, nulls, alignment, empty work
+    assert lib.fp8_quant_mx(A, b.E4M3, 4, 128, b.E4M3, A, A, 0, None) == b.E_DTYPE
+    assert lib.fp8_quant_mx(A, b.BF16, 4, 128, b.BF16, A, A, 0, None) == b.E_DTYPE
+    assert lib.fp8_quant_mx(A, b.BF16, 4, 128, b.E4M3, A, A, 8, None) == b.E_DTYPE
+    assert lib.fp8_quant_mx(A, b.BF16, 4, 48, b.E4M3, A, A, 0, None) == b.E_SHAPE
+    assert lib.fp8_quant_mx(A, b.BF16, 4, 96, b.E4M3, A, A, b.MX_SCALES_PACKED, None) == b.E_SHAPE
+    assert lib.fp8_quant_mx(A, b.BF16, 4, 128, b.E4M3, A, None, 0, None) == b.E_NULL
+    assert lib.fp8_quant_mx(A + 4, b.BF16, 4, 128, b.E4M3, A, A, 0, None) == b.E_ALIGN
+    assert lib.fp8_quant_mx(None, b.BF16, 0, 128, b.E5M2, None, None, 0, None) == b.OK
+    # scale packing
+    assert lib.fp8_pack_mx_scales(A, 4, 96, A, None) == b.E_SHAPE
+    assert lib.fp8_pack_mx_scales(None, 4, 128, A, None) == b.E_NULL
+    assert lib.fp8_pack_mx_scales(None, 0, 128, None, None) == b.OK
+    # GEMM: output dtype, activation format, layout bits, K multiple, nulls, alignment, empty work
+    assert lib.fp8_scaled_gemm_mx(A, A, b.E4M3, A, A, 0, A, b.E4M3, 4, 8, 128, None) == b.E_DTYPE
+    assert lib.fp8_scaled_gemm_mx(A, A, b.BF16, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_DTYPE
+    assert lib.fp8_scaled_gemm_mx(A, A, b.E4M3, A, A, 4, A, b.BF16, 4, 8, 128, None) == b.E_DTYPE
+    assert lib.fp8_scaled_gemm_mx(A, A, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 96, None) == b.E_SHAPE
+    assert lib.fp8_scaled_gemm_mx(A, None, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_NULL
+    assert lib.fp8_scaled_gemm_mx(A, A, b.E4M3, A, A, 0, None, b.BF16, 4, 8, 128, None) == b.E_NULL
+    assert lib.fp8_scaled_gemm_mx(A + 8, A, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_ALIGN
+    assert lib.fp8_scaled_gemm_mx(A, A + 2, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_ALIGN
+    assert lib.fp8_scaled_gemm_mx(None, None, b.E5M2, None, None, 0, None, b.F32, 0, 8, 128, None) == b.OK
+
+
+def pack_mx_codes_reference(q):
+    """The MX fragment order written out from its definition in include/fp8sg.h:
+    codes [R, K] -> ceil(R / 16) * 16 * K bytes; lane l of the 2048-byte block of
+    (16-row tile t, 128-k block kb) holds row 16 t + l % 16, k 128 kb + 16 (l / 16)
+    + [0, 16) at 16 l and k 128 kb + 64 + 16 (l / 16) + [0, 16) at 1024 + 16 l;
+    padding rows 0."""
+    import numpy as np
+    R, K = q.shape
+    rows = (R + 15) // 16 * 16
+    w = np.zeros((rows, K), np.uint8)
+    w[:R] = q
+    nkb = K // 128
+    out = np.zeros(rows * K, np.uint8)
+    for t in range(rows // 16):
+        for kb in range(nkb):
+            base = (t * nkb + kb) * 2048
+            for lane in range(64):
+                r = 16 * t + lane % 16
+                k0 = kb * 128 + 16 * (lane // 16)
+                out[base + lane * 16: base + lane * 16 + 16] = w[r, k0:k0 + 16]
+                out[base + 1024 + lane * 16: base + 1024 + lane * 16 + 16] = w[r, k0 + 64:k0 + 80]
+    return out
+
+
+def test_mx_code_order_is_a_permutation():
+    import numpy as np
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 256, (32, 256), dtype=np.uint8)
+    p = pack_mx_codes_reference(q)
+    assert np.array_equal(np.sort(p), np.sort(q.ravel()))
+    assert np.array_equal(p[:16], q[0, :16]) and np.array_equal(p[1024:1040], q[0, 64:80])
+    assert np.array_equal(p[16 * 17:16 * 18], q[1, 16:32])
