@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline only: skip the detail workloads")
     ap.add_argument("--workload", nargs="*", default=None,
                     help="detail workloads to run (default all): prefill large quant kv weights blockwise fp8out "
-                         "attention")
+                         "attention mx")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -203,7 +203,7 @@ def main():
 
     # ------------------------------------------------------------ details
     wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights", "blockwise",
-                                                       "fp8out", "attention"}
+                                                       "fp8out", "attention", "mx"}
     if args.quick:
         wanted = set()
     del wqs[1:], wrm[1:]
@@ -437,6 +437,61 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
                         "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
                         "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
             del xl, aq, sa, wq, wp, y
+            torch.cuda.empty_cache()
+
+    if "mx" in wanted:
+        log("mxfp8")
+        from workloads import decode_inputs
+        # decode shape: weights quantized offline straight into the packed MX order
+        _, w, _ = decode_inputs(1)
+        w_t = torch.from_numpy(w).to(dev)
+        N, K = w.shape
+        d = timed_events(lambda i: sg.fp8_quant_mx(w_t, layout="packed", scale_layout="packed"), 20, 3, reps=3)
+        out.append({"workload": f"MX weight quant W fp32 [{N},{K}] 32-element blocks (offline)",
+                    "avg_us": round(float(d.mean()) * 1e3, 1), "GB_s": _gbs(5 * N * K + N * K // 32, d.mean())})
+        wp, ws = sg.fp8_quant_mx(w_t, layout="packed", scale_layout="packed")
+        wps = copies(wp, 8)
+        del w_t
+        for m in (1, 8, 32):
+            xb, _, _ = decode_inputs(m, with_weight=False)
+            x = to_bf16(xb)
+            aq, sa = sg.fp8_quant_mx(x, layout="packed", scale_layout="packed")
+            y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            d = timed_events(lambda i: sg.fp8_quant_mx(x, layout="packed", scale_layout="packed", q=aq, scales=sa),
+                             100, 20)
+            out.append({"workload": f"MX act quant X bf16 [{m},{K}]", "avg_us": round(float(d.mean()) * 1e3, 2)})
+            d = timed_events(lambda i: sg.fp8_scaled_gemm_mx(aq, sa, wps[i % 8], ws, y=y, w_layout="packed",
+                                                             a_layout="packed", a_shape=(m, K), w_shape=(N, K)),
+                             100, 20)
+            kb = N * K + ws.numel() + m * K + sa.numel() + 2 * m * N
+            out.append({"workload": f"MX decode GEMM M={m} N={N} K={K}", "accum": "scaled mfma",
+                        "avg_us": round(float(d.mean()) * 1e3, 2), "GB_s": _gbs(kb, d.mean()),
+                        "frac_hbm": round(_gbs(kb, d.mean()) / HBM_PEAK_GBS, 4)})
+        del wps, wp
+        torch.cuda.empty_cache()
+        # prefill shapes, E4M3 and E5M2 activations
+        for K in (4096, 14336):
+            xb, w, _ = prefill_inputs(K)
+            M, N = xb.shape[0], w.shape[0]
+            xl = copies(to_bf16(xb), 2)
+            wp, ws = sg.fp8_quant_mx(torch.from_numpy(w).to(dev), layout="packed", scale_layout="packed")
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for fmt in ("e4m3", "e5m2"):
+                aq, sa = sg.fp8_quant_mx(xl[0], fmt, layout="packed", scale_layout="packed")
+                d = timed_events(lambda i: sg.fp8_quant_mx(xl[i % 2], fmt, layout="packed", scale_layout="packed",
+                                                           q=aq, scales=sa), 20, 3, reps=3)
+                gbs = _gbs(3 * M * K + M * K // 32, d.mean())
+                out.append({"workload": f"MX act quant X bf16 [{M},{K}] {fmt}", "avg_us": round(float(d.mean()) * 1e3, 2),
+                            "GB_s": gbs, "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+                d = timed_events(lambda i: sg.fp8_scaled_gemm_mx(aq, sa, wp, ws, a_fmt=fmt, y=y, w_layout="packed",
+                                                                 a_layout="packed", a_shape=(M, K), w_shape=(N, K)),
+                                 10, 3, reps=3)
+                tf = _tflops(2.0 * M * N * K, d.mean())
+                out.append({"workload": f"MX prefill GEMM {M}x{N}x{K} A {fmt}", "accum": "scaled mfma",
+                            "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
+                            "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
+                del aq, sa
+            del xl, wp, ws, y
             torch.cuda.empty_cache()
 
     if "fp8out" in wanted:

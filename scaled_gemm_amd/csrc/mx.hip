@@ -64,9 +64,9 @@ __device__ __forceinline__ int64_t mx_packed_scale_offset(int64_t r, int b, int6
 // block maximum comes from two lane exchanges, the quotient x / 2^k is the
 // product x * 2^-k (both correctly rounded, so equal), and every |quotient|
 // is at most FMAX, which the hardware converter rounds to nearest even
-// exactly.  Codes go out row-major or in the MX fragment order; the team's
-// first thread writes the scale byte.
-template <typename InT, int kFmt, bool kPackedCodes, bool kPackedScales>
+// exactly.  Codes go out row-major; the team's first thread writes the scale
+// byte (row-major or packed).
+template <typename InT, int kFmt, bool kPackedScales>
 __global__ __launch_bounds__(256) void mx_quant(const InT* __restrict__ x, int64_t R, int K, uint8_t* __restrict__ q,
                                                 uint8_t* __restrict__ sc) {
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -86,15 +86,7 @@ __global__ __launch_bounds__(256) void mx_quant(const InT* __restrict__ x, int64
     uint2 o;
     o.x = pack4<kFmt>(v[0] * rr, v[1] * rr, v[2] * rr, v[3] * rr);
     o.y = pack4<kFmt>(v[4] * rr, v[5] * rr, v[6] * rr, v[7] * rr);
-    if (kPackedCodes) {
-        // MX fragment order: k = 64 h + 16 g + b of the block goes to lane 16 g + r, half h, byte b
-        const int nkb = K >> 7, kb = kk >> 7, hk = kk & 127;
-        const int lane = ((hk & 63) >> 4) * 16 + (int)(r & 15);
-        uint8_t* blk = q + ((r >> 4) * nkb + kb) * kPackBlock;
-        *reinterpret_cast<uint2*>(blk + (hk >> 6) * 1024 + lane * 16 + (hk & 15)) = o;
-    } else {
-        *reinterpret_cast<uint2*>(q + r * K + kk) = o;
-    }
+    *reinterpret_cast<uint2*>(q + r * K + kk) = o;
     if ((kk & 31) == 0) {
         const uint8_t e = (uint8_t)(k + 127);
         if (kPackedScales) sc[mx_packed_scale_offset(r, kk >> 5, (R + 63) >> 6)] = e;
@@ -102,15 +94,84 @@ __global__ __launch_bounds__(256) void mx_quant(const InT* __restrict__ x, int64
     }
 }
 
+// Quantization into the MX fragment order: one wave per (16-row tile, 128-k
+// block), lane l = 16 g + r reads row r's k [16 g, 16 g + 16) and
+// [64 + 16 g, 64 + 16 g + 16) (the two halves of its fragment) and writes them
+// as 16-byte codes at 16 l and 1024 + 16 l, so every store instruction writes
+// one contiguous kilobyte.  The 32-k block of each half is shared with lane
+// l ^ 16 (one exchange); each lane writes one scale byte: block g / 2 of its
+// first half for even g, block 2 + g / 2 of its second half for odd g.  Rows
+// past R read nothing and write no codes.
+template <typename InT, int kFmt, bool kPackedScales>
+__global__ __launch_bounds__(256) void mx_quant_packed(const InT* __restrict__ x, int64_t R, int K,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+    const int lane = threadIdx.x & 63;
+    const int nkb = K >> 7;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (tile, kb), kb fastest
+    const int64_t T = (R + 15) >> 4;
+    if (unit >= T * nkb) return;                                         // whole waves only
+    const int64_t t = unit / nkb;
+    const int kb = (int)(unit - t * nkb);
+    const int g = lane >> 4, r16 = lane & 15;
+    const int64_t r = t * 16 + r16;
+    const bool live = r < R;
+    float v[2][16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (live) {
+            const InT* p = x + r * K + kb * 128 + 64 * h + 16 * g;
+            float c0[8], c1[8];
+            load_chunk<InT>(p, c0);
+            load_chunk<InT>(p + 8, c1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[h][i] = c0[i];
+                v[h][8 + i] = c1[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[h][i] = 0.0f;
+        }
+    }
+    int kx[2];
+    uint8_t* blk = q + (t * nkb + kb) * kPackBlock;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, __builtin_fabsf(v[h][i]));
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        kx[h] = mx_scale_exp<kFmt>(a);
+        const float rr = __uint_as_float((uint32_t)(127 - kx[h]) << 23);
+        uint4 o;
+        o.x = pack4<kFmt>(v[h][0] * rr, v[h][1] * rr, v[h][2] * rr, v[h][3] * rr);
+        o.y = pack4<kFmt>(v[h][4] * rr, v[h][5] * rr, v[h][6] * rr, v[h][7] * rr);
+        o.z = pack4<kFmt>(v[h][8] * rr, v[h][9] * rr, v[h][10] * rr, v[h][11] * rr);
+        o.w = pack4<kFmt>(v[h][12] * rr, v[h][13] * rr, v[h][14] * rr, v[h][15] * rr);
+        if (live) *reinterpret_cast<uint4*>(blk + h * 1024 + lane * 16) = o;
+    }
+    if (live) {
+        const int b = (g & 1) ? 2 + (g >> 1) : (g >> 1);       // this lane's scale: its block in the k block
+        const uint8_t e = (uint8_t)(((g & 1) ? kx[1] : kx[0]) + 127);
+        if (kPackedScales) sc[mx_packed_scale_offset(r, kb * 4 + b, (R + 63) >> 6)] = e;
+        else sc[r * (K >> 5) + kb * 4 + b] = e;
+    }
+}
+
 template <typename InT, int kFmt>
 static void launch_mx_quant_t(const InT* x, int64_t R, int K, uint8_t* q, bool pc, uint8_t* sc, bool ps,
                               hipStream_t stream) {
+    if (pc) {
+        const int64_t units = ((R + 15) >> 4) * (K >> 7);
+        dim3 grid((unsigned)((units + 3) / 4)), block(256);
+        if (ps) mx_quant_packed<InT, kFmt, true><<<grid, block, 0, stream>>>(x, R, K, q, sc);
+        else mx_quant_packed<InT, kFmt, false><<<grid, block, 0, stream>>>(x, R, K, q, sc);
+        return;
+    }
     const int64_t threads = R * (K >> 3);
     dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-    if (pc && ps) mx_quant<InT, kFmt, true, true><<<grid, block, 0, stream>>>(x, R, K, q, sc);
-    else if (pc) mx_quant<InT, kFmt, true, false><<<grid, block, 0, stream>>>(x, R, K, q, sc);
-    else if (ps) mx_quant<InT, kFmt, false, true><<<grid, block, 0, stream>>>(x, R, K, q, sc);
-    else mx_quant<InT, kFmt, false, false><<<grid, block, 0, stream>>>(x, R, K, q, sc);
+    if (ps) mx_quant<InT, kFmt, true><<<grid, block, 0, stream>>>(x, R, K, q, sc);
+    else mx_quant<InT, kFmt, false><<<grid, block, 0, stream>>>(x, R, K, q, sc);
 }
 
 hipError_t launch_mx_quant(const void* x, bool x_is_bf16, int64_t R, int64_t K, int fmt, uint8_t* q,
