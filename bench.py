@@ -48,8 +48,10 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
 # was measured on: when the hash of these files differs, traffic is reported
 # as null until the counters are taken again.
 TRAFFIC = {"kernel": "gemm_skinny<false, 1, 2, 2, 4, 1, true, true, false>",
-           "sources": ("scaled_gemm_amd/csrc/gemm.hip", "scaled_gemm_amd/csrc/fp8_device.h"),
-           "sha256": ("243d51a615c0663e81afa7173ce729b2a9f944665ca885deded376790905ac37",
+           "sources": ("scaled_gemm_amd/csrc/gemm.hip", "scaled_gemm_amd/csrc/gemm_common.h",
+                       "scaled_gemm_amd/csrc/fp8_device.h"),
+           "sha256": ("ce20a349815af3ba332cee9bf33617313b0d7b834fc791c5bee29cb937176ac5",
+                      "7a2516bae919f660ea820fdefe814bf67af917b32a888664e4c14b763ca303c8",
                       "d804fc261e7f9537fe0a5fdc56bf755645872288b5327b561eb758b9f43b6ef0"),
            "fetch_kib": 29258.0, "write_kib": 896.09375,
            "fetch_factor": 1048576.0 / 524299.5, "write_factor": 1048576.0 / 1048576.0}
