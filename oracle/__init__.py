@@ -16,10 +16,12 @@ Modules:
             GEMM that scales each 128-deep partial sum by its own scales
   mx     -- MXFP8: 32-element blocks along k with power-of-two (E8M0)
             scales; the GEMM that scales each 32-deep partial sum
+  norm   -- RMS normalisation (the producer the per-token quantization is
+            fused into)
   attention -- decode attention over an FP8 KV cache with per-head scales
             (standard softmax; the online recurrence, as a pinned statement)
   native -- the same encoder in plain C (oracle/c/fp8_oracle.c) for sweeps
             over every float32 bit pattern; loaded from its built library
 """
 
-from . import attention, blockwise, fp8, kv, mx, w8a8  # noqa: F401
+from . import attention, blockwise, fp8, kv, mx, norm, w8a8  # noqa: F401
