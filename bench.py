@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline only: skip the detail workloads")
     ap.add_argument("--workload", nargs="*", default=None,
                     help="detail workloads to run (default all): prefill large quant kv weights blockwise fp8out "
-                         "attention mx")
+                         "attention mx rmsnorm")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -205,7 +205,7 @@ def main():
 
     # ------------------------------------------------------------ details
     wanted = set(args.workload) if args.workload else {"prefill", "large", "quant", "kv", "weights", "blockwise",
-                                                       "fp8out", "attention", "mx"}
+                                                       "fp8out", "attention", "mx", "rmsnorm"}
     if args.quick:
         wanted = set()
     del wqs[1:], wrm[1:]
@@ -323,7 +323,7 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
         out.append({"workload": f"{tag} {name} X bf16 [{M},{K}]", "avg_us": round(float(d.mean()) * 1e3, 2),
                     "GB_s": gbs, "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "buffers": len(x_list)})
 
-    if "prefill" in wanted or "quant" in wanted:
+    if "prefill" in wanted or "quant" in wanted or "rmsnorm" in wanted:
         for K in (4096, 14336):
             log(f"prefill K={K}")
             xb, w, _ = prefill_inputs(K)
@@ -332,6 +332,17 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
             xl = copies(x0, 4 if K == 4096 else 2)
             if "quant" in wanted:
                 quant_rows(f"prefill K={K}", xl, M, K)
+            if "rmsnorm" in wanted and K == 4096:
+                # RMSNorm of the rows with the per-token quantization fused in (gamma bf16 [K])
+                g = torch.ones(K, dtype=torch.bfloat16, device=dev)
+                qn, sn = sg.fp8_rmsnorm_quant_per_token(xl[0], g, 1e-6)
+                d = timed_events(lambda i: sg.fp8_rmsnorm_quant_per_token(xl[i % len(xl)], g, 1e-6, q=qn, scales=sn),
+                                 20, 3, reps=3)
+                gbs = _gbs(3 * M * K + 2 * K + 4 * M, d.mean())
+                out.append({"workload": f"RMSNorm + per-token quant X bf16 [{M},{K}] (fused)",
+                            "avg_us": round(float(d.mean()) * 1e3, 2), "GB_s": gbs,
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "buffers": len(xl)})
+                del qn, sn
             if "prefill" in wanted:
                 wq, sw = sg.fp8_quant_weight_per_channel(torch.from_numpy(w).to(dev))
                 gemm_rows(f"prefill K={K}", xl, wq, sw, M, N, K)

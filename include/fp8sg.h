@@ -225,6 +225,28 @@ fp8sg_status fp8_scaled_gemm_fp8out(const void* a, int a_dtype, float* a_scales,
                                     int accum, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * RMSNorm with the per-token activation quantization fused into it (FP8
+ * Inference Explained, in depth -- "Scales and their granularity": engines
+ * fuse the per-token amax reduction into the kernel that produces the
+ * activations; here that producer is the RMS normalisation in front of a
+ * transformer's linear layers).  For each row, in fp32:
+ *   ss = sum_k x_k^2, r = 1 / sqrt(ss / K + eps), y_k = (x_k * r) * gamma_k,
+ * then the dynamic per-token rule on y: s = RN32(max_k |y_k| / 448) (1.0 when
+ * 0), q_k = E4M3(RN32(y_k / s)).  The codes and the scale are exactly those
+ * rules applied to the fp32 y the call writes to y_out.
+ *   x       [M, K] FP8SG_BF16 or FP8SG_F32;  gamma [K], the same dtype
+ *   eps     finite, >= 0
+ *   q       [M, K] E4M3 codes, or with layout FP8SG_A_PACKED the fragment
+ *           order of fp8_pack_weights (padding rows unwritten)
+ *   scales  [M] fp32 (output)
+ *   y_out   [M, K] fp32 normalised rows (output), or NULL
+ *   0 < K <= 16384, K % 16 == 0 (K % 128 == 0 when packed).
+ */
+fp8sg_status fp8_rmsnorm_quant_per_token(const void* x, int x_dtype, const void* gamma, float eps, int64_t M,
+                                         int64_t K, uint8_t* q, float* scales, float* y_out, int layout,
+                                         void* stream);
+
+/*
  * Block-wise dynamic activation quantization: one scale per token and group of
  * 128 consecutive k, so an outlier widens the step of its own group only (FP8
  * Quantization notebook -- "Granularity"; FP8 Inference Explained, in depth --

@@ -31,6 +31,7 @@ from .fp8sg import (  # noqa: F401
     fp8_pack_weights,
     fp8_packed_weight_bytes,
     fp8_quant_mx,
+    fp8_rmsnorm_quant_per_token,
     fp8_quant_per_tensor_static,
     fp8_quant_per_token_group,
     fp8_quant_weight_blockwise,

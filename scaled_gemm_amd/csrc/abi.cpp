@@ -284,6 +284,24 @@ fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales
                                                  M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, (hipStream_t)stream));
 }
 
+fp8sg_status fp8_rmsnorm_quant_per_token(const void* x, int x_dtype, const void* gamma, float eps, int64_t M,
+                                         int64_t K, uint8_t* q, float* scales, float* y_out, int layout,
+                                         void* stream) {
+    if (!is_hp(x_dtype)) return FP8SG_E_DTYPE;
+    if (layout != 0 && layout != FP8SG_A_PACKED) return FP8SG_E_DTYPE;
+    if (M < 0 || K < 0 || M >= kMaxDim || K > 16384 || K % (layout ? 128 : 16) != 0) return FP8SG_E_SHAPE;
+    if (!(eps >= 0.0f) || eps == __builtin_inff()) return FP8SG_E_SHAPE;
+    if (M == 0) return FP8SG_OK;
+    if (K == 0) return FP8SG_E_SHAPE;  // the mean of an empty row is undefined
+    if (!x || !gamma || !q || !scales) return FP8SG_E_NULL;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8SG_E_ALIGN;
+    if (y_out && !aligned(y_out, 16)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    return launched(fp8sg::launch_rmsnorm_quant(x, x_dtype == FP8SG_BF16, gamma, eps, M, K, q, scales, y_out,
+                                                layout == FP8SG_A_PACKED, (hipStream_t)stream));
+}
+
 size_t fp8_mx_packed_scale_bytes(int64_t rows, int64_t K) {
     if (rows <= 0 || K <= 0) return 0;
     return (size_t)((rows + 63) / 64) * 256 * (size_t)(K / 128);

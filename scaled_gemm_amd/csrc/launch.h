@@ -16,6 +16,11 @@ constexpr int kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2;
 hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
                             bool packed, hipStream_t stream);
 
+// RMSNorm fused with per-token E4M3 quantization of its output (K <= 16384);
+// gamma has x's dtype; y_out (optional) receives the fp32 normalised rows.
+hipError_t launch_rmsnorm_quant(const void* x, bool x_is_bf16, const void* gamma, float eps, int64_t M, int64_t K,
+                                uint8_t* q, float* scales, float* y_out, bool packed, hipStream_t stream);
+
 // Block-wise dynamic quantization: activations in 1 x 128 groups (scales [M, K/128]),
 // weights in 128 x 128 blocks (scales [ceil(N/128), K/128]); K % 128 == 0.
 hipError_t launch_group_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,

@@ -123,6 +123,111 @@ hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
+// RMSNorm with the per-token quantization fused into it: the quantizer's
+// maximum is taken over the normalised row while it is still in registers, so
+// the bf16 normalised activations are never written and read back (the pages'
+// engines fuse the amax reduction into the preceding kernel).
+//   ss = sum_k x_k^2 (fp32 fused multiply-adds over each thread's chunks in
+//   order, then the wave tree, then the four waves in a fixed order),
+//   r = RN32(1 / RN32(sqrt(RN32(RN32(ss / K) + eps)))),
+//   y_k = RN32(RN32(x_k * r) * g_k), then the dynamic per-token rule on y.
+// y_out (optional) receives y in fp32.  One workgroup per row, the row in
+// registers (K <= 16384), as in row_quant_resident.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const float t = (red[0] + red[1]) + (red[2] + red[3]);   // 4 waves, fixed order
+    __syncthreads();
+    return t;
+}
+
+template <typename InT, int kChunks, bool kPacked>
+__global__ __launch_bounds__(256) void rmsnorm_quant(const InT* __restrict__ x, const InT* __restrict__ gamma,
+                                                     float eps, int64_t K, uint8_t* __restrict__ q,
+                                                     float* __restrict__ scales, float* __restrict__ y_out) {
+    __shared__ float red[4];
+    const int t = (int)threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const InT* xr = x + row * K;
+    const int nchunks = (int)(K >> 3);
+    float v[kChunks][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int c = t + i * 256;
+        if (c < nchunks) {
+            load_chunk<InT>(xr + (int64_t)c * 8, v[i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(v[i][j], v[i][j], ss);
+        }
+    }
+    ss = block_sum(ss, red);
+    const float r = 1.0f / __builtin_sqrtf(ss / (float)K + eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int c = t + i * 256;
+        if (c < nchunks) {
+            float g[8];
+            load_chunk<InT>(gamma + (int64_t)c * 8, g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                v[i][j] = (v[i][j] * r) * g[j];
+                amax = fmaxf(amax, __builtin_fabsf(v[i][j]));
+            }
+            if (y_out) {
+                float4* yo = reinterpret_cast<float4*>(y_out + row * K + (int64_t)c * 8);
+                yo[0] = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+                yo[1] = make_float4(v[i][4], v[i][5], v[i][6], v[i][7]);
+            }
+        }
+    }
+    amax = block_max(amax, red);
+    const float s = dynamic_scale(amax, kE4M3Max);
+    if (t == 0) scales[row] = s;
+    const QScale p = make_qscale(s, kE4M3Max);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int c = t + i * 256;
+        if (c < nchunks) {
+            uint8_t* dst = kPacked ? q + packed_offset(row, (int64_t)c * 8, K >> 7) : q + row * K + (int64_t)c * 8;
+            *reinterpret_cast<uint2*>(dst) = encode_chunk_dynamic<float>(v[i], p);
+        }
+    }
+}
+
+template <typename InT, bool kPacked>
+static void launch_rmsnorm_quant_t(const InT* x, const InT* g, float eps, int64_t M, int64_t K, uint8_t* q,
+                                   float* scales, float* y_out, hipStream_t stream) {
+    const int64_t per = (K / 8 + 255) / 256;
+    dim3 grid((unsigned)M), block(256);
+    if (per <= 1) rmsnorm_quant<InT, 1, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
+    else if (per <= 2) rmsnorm_quant<InT, 2, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
+    else if (per <= 4) rmsnorm_quant<InT, 4, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
+    else rmsnorm_quant<InT, 8, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
+}
+
+hipError_t launch_rmsnorm_quant(const void* x, bool x_is_bf16, const void* gamma, float eps, int64_t M, int64_t K,
+                                uint8_t* q, float* scales, float* y_out, bool packed, hipStream_t stream) {
+    if (M == 0) return hipSuccess;
+    if (x_is_bf16) {
+        if (packed) launch_rmsnorm_quant_t<uint16_t, true>((const uint16_t*)x, (const uint16_t*)gamma, eps, M, K, q,
+                                                           scales, y_out, stream);
+        else launch_rmsnorm_quant_t<uint16_t, false>((const uint16_t*)x, (const uint16_t*)gamma, eps, M, K, q, scales,
+                                                     y_out, stream);
+    } else {
+        if (packed) launch_rmsnorm_quant_t<float, true>((const float*)x, (const float*)gamma, eps, M, K, q, scales,
+                                                        y_out, stream);
+        else launch_rmsnorm_quant_t<float, false>((const float*)x, (const float*)gamma, eps, M, K, q, scales, y_out,
+                                                  stream);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Block-wise dynamic quantization.
 //
 // Activations, one scale per (row, 128-element group): a group is 16 chunks of

@@ -62,6 +62,7 @@ _SIGS = {
     "fp8_quant_per_token_group": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]),
     "fp8_quant_weight_blockwise": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_blockwise": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
+    "fp8_rmsnorm_quant_per_token": (_i32, [_vp, _i32, _vp, ctypes.c_float, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "fp8_mx_packed_scale_bytes": (_sz, [_i64, _i64]),
     "fp8_quant_mx": (_i32, [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _i32, _vp]),
     "fp8_pack_mx_scales": (_i32, [_vp, _i64, _i64, _vp, _vp]),
@@ -333,6 +334,30 @@ def fp8_scaled_gemm_blockwise(a: torch.Tensor, a_scales: torch.Tensor, wq: torch
     _check(lib().fp8_scaled_gemm_blockwise(_ptr(a), _ptr(a_scales), _ptr(wq), layout, _ptr(w_scales), _ptr(y), y_code,
                                            M, N, K, _ACCUM[accum], _stream(stream)), "fp8_scaled_gemm_blockwise")
     return y
+
+
+def fp8_rmsnorm_quant_per_token(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, layout="row_major",
+                                q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                                y_out: Optional[torch.Tensor] = None, stream=None):
+    """RMSNorm(x) * gamma quantized per token in one pass: x [M, K] (bf16/fp32),
+    gamma [K] (same dtype) -> (codes, scales [M] fp32).  layout="packed": the
+    codes in the fragment order (1-D).  y_out: optional [M, K] fp32 tensor that
+    receives the normalised rows."""
+    _need(x, "x", _HP)
+    M, K = x.shape
+    _need(gamma, "gamma", (x.dtype,), (K,))
+    packed = _LAYOUT[layout] == W_PACKED
+    qshape = (fp8_packed_weight_bytes(M, K),) if packed else (M, K)
+    q = torch.empty(qshape, dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty(M, dtype=torch.float32, device=x.device) if scales is None else scales
+    _need(q, "q", (torch.uint8,), qshape)
+    _need(scales, "scales", (torch.float32,), (M,))
+    if y_out is not None:
+        _need(y_out, "y_out", (torch.float32,), (M, K))
+    _check(lib().fp8_rmsnorm_quant_per_token(_ptr(x), _hp_code(x), _ptr(gamma), float(eps), M, K, _ptr(q),
+                                             _ptr(scales), _ptr(y_out), A_PACKED if packed else 0, _stream(stream)),
+           "fp8_rmsnorm_quant_per_token")
+    return q, scales
 
 
 def fp8_mx_packed_scale_bytes(rows: int, K: int) -> int:
