@@ -88,7 +88,10 @@ hipError_t launch_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t
     if (numel > 0) {
         const int64_t nunits = numel / 16, d_units = D / 16, period = d_units * H;
         int64_t blocks = (nunits + 255) / 256;
-        const int64_t cap = 256 * 16;
+        // four workgroups per CU, each looping over its share: more workgroups
+        // only add atomics at the end (measured: 1024 -> 90 us, 4096 -> 103 us,
+        // 8192 -> 129 us for bf16 [8, 32768, 8, 128])
+        const int64_t cap = 1024;
         if (blocks > cap) blocks = cap;
         // make the stride a multiple of the head period when possible
         const int64_t stride = blocks * 256;
@@ -130,9 +133,10 @@ hipError_t launch_kv_dequant(const uint8_t* kvq, int64_t numel, int64_t H, int64
                              int fmt, uint16_t* out, hipStream_t stream) {
     if (numel == 0) return hipSuccess;
     const int64_t nunits = numel / 16;
+    // one unit per thread (the loop only strides past 2^31 workgroups): a grid
+    // capped at 16 workgroups per CU ran at 4.5 TB/s, the full grid at 5.9 TB/s
     int64_t blocks = (nunits + 255) / 256;
-    const int64_t cap = 256 * 16;
-    if (blocks > cap) blocks = cap;
+    if (blocks > ((int64_t)1 << 31) - 1) blocks = ((int64_t)1 << 31) - 1;
     if (fmt == 0) kv_dequant<0><<<(unsigned)blocks, 256, 0, stream>>>(kvq, nunits, D / 16, (int)H, head_scales, out);
     else kv_dequant<1><<<(unsigned)blocks, 256, 0, stream>>>(kvq, nunits, D / 16, (int)H, head_scales, out);
     return hipGetLastError();
