@@ -324,3 +324,18 @@ def test_mx_code_order_is_a_permutation():
     assert np.array_equal(np.sort(p), np.sort(q.ravel()))
     assert np.array_equal(p[:16], q[0, :16]) and np.array_equal(p[1024:1040], q[0, 64:80])
     assert np.array_equal(p[16 * 17:16 * 18], q[1, 16:32])
+
+
+def test_rmsnorm_quant_validation(lib):
+    f = lib.fp8_rmsnorm_quant_per_token
+    assert f(A, b.E4M3, A, 1e-6, 4, 128, A, A, None, 0, None) == b.E_DTYPE
+    assert f(A, b.BF16, A, 1e-6, 4, 128, A, A, None, b.W_PACKED, None) == b.E_DTYPE
+    assert f(A, b.BF16, A, 1e-6, 4, 20000, A, A, None, 0, None) == b.E_SHAPE       # K beyond 16384
+    assert f(A, b.BF16, A, 1e-6, 4, 24, A, A, None, 0, None) == b.E_SHAPE          # K % 16
+    assert f(A, b.BF16, A, 1e-6, 4, 144, A, A, None, b.A_PACKED, None) == b.E_SHAPE  # K % 128 when packed
+    assert f(A, b.BF16, A, -1.0, 4, 128, A, A, None, 0, None) == b.E_SHAPE         # eps < 0
+    assert f(A, b.BF16, A, float("inf"), 4, 128, A, A, None, 0, None) == b.E_SHAPE
+    assert f(A, b.BF16, A, 1e-6, 4, 0, A, A, None, 0, None) == b.E_SHAPE           # empty rows
+    assert f(A, b.BF16, None, 1e-6, 4, 128, A, A, None, 0, None) == b.E_NULL
+    assert f(A, b.BF16, A, 1e-6, 4, 128, A, A, A + 4, 0, None) == b.E_ALIGN
+    assert f(None, b.BF16, None, 1e-6, 0, 128, None, None, None, 0, None) == b.OK
