@@ -50,10 +50,10 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
 TRAFFIC = {"kernel": "gemm_skinny<false, 1, 2, 2, 4, 1, true, true, false>",
            "sources": ("scaled_gemm_amd/csrc/gemm.hip", "scaled_gemm_amd/csrc/gemm_common.h",
                        "scaled_gemm_amd/csrc/fp8_device.h"),
-           "sha256": ("ce20a349815af3ba332cee9bf33617313b0d7b834fc791c5bee29cb937176ac5",
-                      "7a2516bae919f660ea820fdefe814bf67af917b32a888664e4c14b763ca303c8",
-                      "d804fc261e7f9537fe0a5fdc56bf755645872288b5327b561eb758b9f43b6ef0"),
-           "fetch_kib": 29258.0, "write_kib": 896.09375,
+           "sha256": ("2286515682f209bffa5555dd6ee84a1cdb21a808b35ca6813e5a2526fd0f14ca",
+                      "1786e96bd0e750e4a92392ae3aea670a9bc9c562537f000921fded2e851d5cfc",
+                      "dddf2e1dade7862522a15f56f2e066096608bc035e0910256e6699782dff88db"),
+           "fetch_kib": 29258.0, "write_kib": 896.0,
            "fetch_factor": 1048576.0 / 524299.5, "write_factor": 1048576.0 / 1048576.0}
 DEC_N, DEC_K = 14336, 4096
 DEC_MS = (1, 8, 32)

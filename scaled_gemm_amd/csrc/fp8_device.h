@@ -154,9 +154,32 @@ __device__ __forceinline__ float dynamic_scale(float amax, float fmax) {
     return s == 0.0f ? 1.0f : s;
 }
 
+// A 16-byte load with the non-temporal hint, for operands that a kernel
+// streams through once (their lines need not stay in the caches).
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // A chunk is 8 consecutive elements: one 16-byte load for bf16, two for fp32.
 template <typename InT>
 __device__ __forceinline__ void load_chunk(const InT* p, float (&v)[8]);
+
+// The same with streaming loads.
+template <typename InT>
+__device__ __forceinline__ void load_chunk_stream(const InT* p, float (&v)[8]) {
+    const uint4 a = load16_stream(p);
+    if constexpr (sizeof(InT) == 2) {
+        v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+        v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+    } else {
+        const uint4 b = load16_stream(p + 4);
+        v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z);
+        v[3] = __uint_as_float(a.w); v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+        v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    }
+}
 
 template <>
 __device__ __forceinline__ void load_chunk<uint16_t>(const uint16_t* p, float (&v)[8]) {

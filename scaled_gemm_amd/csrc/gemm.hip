@@ -136,7 +136,8 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
             const int64_t off = (int64_t)kb << 7;
 #pragma unroll
             for (int s = 0; s < kNS; ++s)
-                wx[s] = kWPacked ? load_frag_packed(wrow[s] + kb * kPackBlock, lane) : load_frag_global(wrow[s] + off);
+                wx[s] = kWPacked ? load_frag_packed_stream(wrow[s] + kb * kPackBlock, lane)
+                                  : load_frag_global(wrow[s] + off);
 #pragma unroll
             for (int t = 0; t < kMT; ++t)
                 ax[t] = kAPacked ? load_frag_packed(arow[t] + kb * kPackBlock, lane) : load_frag_global(arow[t] + off);
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
                 const int64_t off = (int64_t)kb << 7;
 #pragma unroll
                 for (int s = 0; s < kNS; ++s)
-                    wf[d][s] = kWPacked ? load_frag_packed(wrow[s] + kb * kPackBlock, lane)
+                    wf[d][s] = kWPacked ? load_frag_packed_stream(wrow[s] + kb * kPackBlock, lane)
                                         : load_frag_global(wrow[s] + off);
 #pragma unroll
                 for (int t = 0; t < kMT; ++t)
@@ -900,7 +901,7 @@ __global__ __launch_bounds__(64 * kKS) __attribute__((amdgpu_waves_per_eu(4))) v
         kb = kb < nkb ? kb : nkb - 1;  // a wave without blocks (nper == 0) loads block nkb - 1, unused
 #pragma unroll
         for (int s = 0; s < kNS; ++s)
-            wf[j][s] = kWPacked ? load_frag_packed(wrow[s] + kb * kPackBlock, lane)
+            wf[j][s] = kWPacked ? load_frag_packed_stream(wrow[s] + kb * kPackBlock, lane)
                                 : load_frag_global(wrow[s] + ((int64_t)kb << 7));
     }
 

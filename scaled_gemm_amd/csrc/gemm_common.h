@@ -63,6 +63,17 @@ __device__ __forceinline__ Frag load_frag_packed(const uint8_t* block, int lane)
     return f;
 }
 
+// Streaming loads of packed weight blocks in the decode kernels: every weight
+// byte is used once per call, so the loads carry the non-temporal hint and do
+// not displace the activations that every workgroup re-reads from L2.  (On
+// row-major weights the hint measured slower, so those loads do without it.)
+__device__ __forceinline__ Frag load_frag_packed_stream(const uint8_t* block, int lane) {
+    Frag f;
+    f.lo = load16_stream(block + 16 * lane);
+    f.hi = load16_stream(block + 1024 + 16 * lane);
+    return f;
+}
+
 // Output kinds (kOutF32 / kOutBF16 / kOutE4M3, launch.h): for E4M3 the code of
 // the fp32 result y is FMT(RN32(y / s_out)) with the given per-tensor output
 // scale s_out, saturating -- the input of a next layer that takes static

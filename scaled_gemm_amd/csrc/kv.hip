@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void kv_dequant(const uint8_t* __restrict__ q,
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += stride) {
         const float s = scales[(u / d_units) % H];
-        const uint4 c = reinterpret_cast<const uint4*>(q)[u];
+        const uint4 c = load16_stream(q + (u << 4));  // codes are read once
         const uint32_t w[4] = {c.x, c.y, c.z, c.w};
         uint32_t o[8];
 #pragma unroll

@@ -317,7 +317,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_mx(const uint8_t* __restrict_
         const int64_t off = (int64_t)kb << 7;
 #pragma unroll
         for (int s = 0; s < kNS; ++s)
-            wx[s] = kWPacked ? load_frag_packed(wrow[s] + kb * kPackBlock, lane) : load_frag_mx_global(wrow[s] + off);
+            wx[s] = kWPacked ? load_frag_packed_stream(wrow[s] + kb * kPackBlock, lane)
+                              : load_frag_mx_global(wrow[s] + off);
 #pragma unroll
         for (int t = 0; t < kMT; ++t)
             ax[t] = kAPacked ? load_frag_packed(arow[t] + kb * kPackBlock, lane) : load_frag_mx_global(arow[t] + off);

@@ -35,7 +35,9 @@ __device__ __forceinline__ int64_t packed_offset(int64_t m, int64_t k, int64_t n
 
 // kChunks chunks per thread held in registers (row length <= kChunks * 8 * blockDim).
 // kPacked: the codes go to the fragment order (packed_offset) instead of [M, K].
-template <typename InT, int kChunks, bool kPacked>
+// kStream: X is read with streaming loads (chosen for large inputs, where it
+// measured 3-7% faster; for decode-sized rows it measured slightly slower).
+template <typename InT, int kChunks, bool kPacked, bool kStream>
 __global__ __launch_bounds__(256) void row_quant_resident(const InT* __restrict__ x, int64_t K,
                                                           uint8_t* __restrict__ q, float* __restrict__ scales) {
     __shared__ float red[4];
@@ -50,7 +52,8 @@ __global__ __launch_bounds__(256) void row_quant_resident(const InT* __restrict_
     for (int i = 0; i < kChunks; ++i) {
         const int c = threadIdx.x + i * T;
         if (c < nchunks) {
-            load_chunk<InT>(xr + (int64_t)c * 8, v[i]);
+            if (kStream) load_chunk_stream<InT>(xr + (int64_t)c * 8, v[i]);
+            else load_chunk<InT>(xr + (int64_t)c * 8, v[i]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(v[i][j]));
         }
@@ -104,11 +107,18 @@ static hipError_t launch_row_quant_t(const InT* x, int64_t M, int64_t K, uint8_t
     const int T = 256;
     const int64_t per = (nchunks + T - 1) / T;
     dim3 grid((unsigned)M), block(T);
-    if (per <= 1) row_quant_resident<InT, 1, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
-    else if (per <= 2) row_quant_resident<InT, 2, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
-    else if (per <= 4) row_quant_resident<InT, 4, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
-    else if (per <= 8) row_quant_resident<InT, 8, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
+    const bool big = M * K * (int64_t)sizeof(InT) >= ((int64_t)16 << 20);
+#define FP8SG_RQ(C)                                                                             \
+    do {                                                                                        \
+        if (big) row_quant_resident<InT, C, kPacked, true><<<grid, block, 0, stream>>>(x, K, q, scales);  \
+        else row_quant_resident<InT, C, kPacked, false><<<grid, block, 0, stream>>>(x, K, q, scales);     \
+    } while (0)
+    if (per <= 1) FP8SG_RQ(1);
+    else if (per <= 2) FP8SG_RQ(2);
+    else if (per <= 4) FP8SG_RQ(4);
+    else if (per <= 8) FP8SG_RQ(8);
     else row_quant_stream<InT, kPacked><<<grid, block, 0, stream>>>(x, K, q, scales);
+#undef FP8SG_RQ
     return hipGetLastError();
 }
 
