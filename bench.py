@@ -48,10 +48,10 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
 # was measured on: when the hash of these files differs, traffic is reported
 # as null until the counters are taken again.
 TRAFFIC = {"kernel": "gemm_skinny<false, 1, 2, 2, 4, 1, true, true, false>",
-           "sources": ("scaled_gemm_amd/csrc/gemm.hip", "scaled_gemm_amd/csrc/gemm_common.h",
+           "sources": ("scaled_gemm_amd/csrc/gemm_skinny.hip", "scaled_gemm_amd/csrc/gemm_common.h",
                        "scaled_gemm_amd/csrc/fp8_device.h"),
-           "sha256": ("2286515682f209bffa5555dd6ee84a1cdb21a808b35ca6813e5a2526fd0f14ca",
-                      "1786e96bd0e750e4a92392ae3aea670a9bc9c562537f000921fded2e851d5cfc",
+           "sha256": ("797e72980ff2a80d55ab2b6d8d479b1ac2618f76b2ac0332abc0c4afae61d362",
+                      "41395d68af2d7059e0ef78463da4775bd83523ac38644413ba143f67d566b4d5",
                       "dddf2e1dade7862522a15f56f2e066096608bc035e0910256e6699782dff88db"),
            "fetch_kib": 29258.0, "write_kib": 896.0,
            "fetch_factor": 1048576.0 / 524299.5, "write_factor": 1048576.0 / 1048576.0}

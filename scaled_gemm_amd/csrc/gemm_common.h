@@ -1,12 +1,27 @@
-// Building blocks shared by the GEMM kernels (gemm.hip, mx.hip): matrix-core
-// fragments, epilogue stores, the LDS copy machinery and tile order of the
-// large-tile kernels, and their staged epilogue.
+// Building blocks shared by the GEMM kernels (gemm_skinny.hip, gemm_big.hip,
+// mx.hip): matrix-core fragments, epilogue stores, the LDS copy machinery and
+// tile order of the large-tile kernels, and their staged epilogue.
 #pragma once
 
 #include "fp8_device.h"
 #include "launch.h"
 
 namespace fp8sg {
+
+// Launchers of the two kernel families, called by the dispatch in gemm.hip:
+// the skinny kernels (gemm_skinny.hip, M <= 32) and the large-tile kernels
+// (gemm_big.hip, M > 32).  Shapes are validated by the caller.
+hipError_t launch_skinny_gemm(const uint8_t* aq, bool a_packed, const float* sa, int sa_per_token, const uint8_t* wq,
+                              bool w_packed, const float* sw, void* y, int out_kind, const float* out_scale, int M,
+                              int N, int K, bool fp8_mfma, hipStream_t stream);
+hipError_t launch_skinny_blockwise(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq,
+                                   bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
+                                   bool fp8_mfma, hipStream_t stream);
+hipError_t launch_big_gemm(const uint8_t* aq, bool a_packed, const float* sa, int sa_per_token, const uint8_t* wq,
+                           bool w_packed, const float* sw, void* y, int out_kind, const float* out_scale, int M, int N,
+                           int K, bool fp8_mfma, hipStream_t stream);
+hipError_t launch_big_blockwise(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq, bool w_packed,
+                                const float* sw, void* y, bool y_bf16, int M, int N, int K, hipStream_t stream);
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -1,0 +1,529 @@
+// Decode-shaped FP8 W8A8 GEMM kernels for gfx950 (M <= 32): the skinny kernel
+// that streams W from HBM straight into registers (per-token / per-tensor and
+// block-wise scales), and the variant with the per-token activation
+// quantization fused in.  Operand roles, the k assignment of a lane and the two
+// accumulation modes are described at the top of gemm.hip.
+#include "gemm_common.h"
+
+#ifndef SKINNY_NS
+#define SKINNY_NS 2
+#endif
+#ifndef SKINNY_KS
+#define SKINNY_KS 4
+#endif
+#ifndef SKINNY_DEPTH
+#define SKINNY_DEPTH 1
+#endif
+
+namespace fp8sg {
+
+// ---------------------------------------------------------------------------
+// Skinny GEMM (M <= 16 * kMT), the decode shape: every byte of W is used once,
+// so W streams from HBM straight into registers.  Every workgroup reads all of
+// A (from L2); in the fragment order (kAPacked) each fragment half is one
+// contiguous kilobyte instead of 64-byte pieces of 16 rows, which halves the
+// cache lines touched per load.  A workgroup owns kNS 16-row
+// subtiles of W; its kKS waves split the k blocks round-robin (wave w takes
+// blocks w, w + kKS, ...).  With kDepth = 1 the loop is software-pipelined: the
+// loads of a wave's next block are issued before its current block is
+// multiplied.  Otherwise (and for block-wise scales) each wave issues the loads
+// of kDepth of its blocks back to back, then multiplies them.  The loop bodies
+// have no branches around loads (rows past M or N are clamped to the last valid
+// row and masked in the epilogue), which lets the compiler wait for each
+// block's loads separately.  The kKS partial sums
+// are added in a fixed order through LDS, so the result does not depend on
+// timing.
+//
+// kBlock: block-wise scales, sa [M, K / 128] and sw [ceil(N / 128), K / 128].
+// Each k block's 16 x 16 partial products start from zero, are multiplied by
+// s_a[m, kb] * s_w[n / 128, kb] and added to the fp32 accumulator, so the
+// epilogue only rounds.  A 16-row subtile never straddles a 128-row block.
+template <bool kFp8, int kOut, int kMT, int kNS, int kKS, int kDepth, bool kWPacked, bool kAPacked,
+          bool kBlock = false>
+__global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
+                                                        int sa_per_token, const uint8_t* __restrict__ W,
+                                                        const float* __restrict__ sw, void* __restrict__ Y, int M,
+                                                        int N, int K, const float* __restrict__ qs) {
+    // Software pipelining pays in exact mode (M = 32: 15.0 -> 14.3 us at N = 14336,
+    // K = 4096) and is neutral for one m-tile; FP8 mode with two m-tiles is 3% slower
+    // with it, so that case keeps the plain loop.
+    constexpr bool kPipe = !kBlock && kDepth == 1 && !(kFp8 && kMT > 1);
+    __shared__ f32x4 red[kKS > 1 ? kKS - 1 : 1][kNS * kMT][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * kNS);
+    const int nkb = K >> 7;
+    const int r16 = lane & 15, kofs = (lane >> 4) * 32;
+
+    // row-major: this lane's row of each subtile; packed: the subtile's first block
+    const uint8_t* wrow[kNS];
+    const int64_t last_tile = ((int64_t)N + 15) / 16 - 1;
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+        if (kWPacked) {
+            int64_t t = (n_base >> 4) + s;
+            t = t < last_tile ? t : last_tile;
+            wrow[s] = W + t * nkb * kPackBlock;
+        } else {
+            int64_t n = n_base + 16 * s + r16;
+            n = n < N ? n : N - 1;
+            wrow[s] = W + n * (int64_t)K + kofs;
+        }
+    }
+    // row-major: this lane's row of each m-tile; packed: the m-tile's first block
+    const uint8_t* arow[kMT];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+        if (kAPacked) {
+            arow[t] = A + (int64_t)t * nkb * kPackBlock;
+        } else {
+            int m = 16 * t + r16;
+            m = m < M ? m : M - 1;
+            arow[t] = A + (int64_t)m * K + kofs;
+        }
+    }
+
+    f32x4 acc[kNS][kMT];
+#pragma unroll
+    for (int s = 0; s < kNS; ++s)
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // block-wise scales: this lane's rows of s_a and the subtiles' rows of s_w
+    const float* sa_row[kMT];
+    const float* sw_row[kNS];
+    if (kBlock) {
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) {
+            const int m = 16 * t + r16 < M ? 16 * t + r16 : M - 1;
+            sa_row[t] = sa + (int64_t)m * nkb;
+        }
+#pragma unroll
+        for (int s = 0; s < kNS; ++s) {
+            const int64_t n = n_base + 16 * s < N ? n_base + 16 * s : N - 1;
+            sw_row[s] = sw + (n >> 7) * nkb;
+        }
+    }
+
+    // this wave's blocks: wave + j * kKS, j < nper
+    const int nper = nkb > wave ? (nkb - wave + kKS - 1) / kKS : 0;
+    if constexpr (kPipe) {
+        // One block in registers while the next block's loads are in flight.  The
+        // scheduling barriers keep the compiler from sinking those loads below the
+        // multiplies (it otherwise issues them at the end of the loop body, which
+        // serialises load latency and matrix work again).
+        auto load_block = [&](int j, Frag (&wx)[kNS], Frag (&ax)[kMT]) {
+            const int kb = wave + j * kKS;
+            const int64_t off = (int64_t)kb << 7;
+#pragma unroll
+            for (int s = 0; s < kNS; ++s)
+                wx[s] = kWPacked ? load_frag_packed_stream(wrow[s] + kb * kPackBlock, lane)
+                                  : load_frag_global(wrow[s] + off);
+#pragma unroll
+            for (int t = 0; t < kMT; ++t)
+                ax[t] = kAPacked ? load_frag_packed(arow[t] + kb * kPackBlock, lane) : load_frag_global(arow[t] + off);
+        };
+        auto mul_block = [&](const Frag (&wx)[kNS], const Frag (&ax)[kMT]) {
+#pragma unroll
+            for (int s = 0; s < kNS; ++s)
+#pragma unroll
+                for (int t = 0; t < kMT; ++t) acc[s][t] = mma<kFp8>(wx[s], ax[t], acc[s][t]);
+        };
+        if (nper > 0) {
+            Frag wf[kNS], af[kMT];
+            load_block(0, wf, af);
+            for (int j = 0; j + 1 < nper; ++j) {
+                Frag wn[kNS], an[kMT];
+                load_block(j + 1, wn, an);
+                __builtin_amdgcn_sched_barrier(0);
+                mul_block(wf, af);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int s = 0; s < kNS; ++s) wf[s] = wn[s];
+#pragma unroll
+                for (int t = 0; t < kMT; ++t) af[t] = an[t];
+            }
+            mul_block(wf, af);
+        }
+    } else {
+        for (int j0 = 0; j0 < nper; j0 += kDepth) {
+            Frag wf[kDepth][kNS], af[kDepth][kMT];
+            float fa[kDepth][kMT], fw[kDepth][kNS];
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                int j = j0 + d;
+                j = j < nper ? j : nper - 1;  // a clamped (repeated) block past the end is loaded but not used
+                const int kb = wave + j * kKS;
+                const int64_t off = (int64_t)kb << 7;
+#pragma unroll
+                for (int s = 0; s < kNS; ++s)
+                    wf[d][s] = kWPacked ? load_frag_packed_stream(wrow[s] + kb * kPackBlock, lane)
+                                        : load_frag_global(wrow[s] + off);
+#pragma unroll
+                for (int t = 0; t < kMT; ++t)
+                    af[d][t] = kAPacked ? load_frag_packed(arow[t] + kb * kPackBlock, lane)
+                                        : load_frag_global(arow[t] + off);
+                if (kBlock) {
+#pragma unroll
+                    for (int t = 0; t < kMT; ++t) fa[d][t] = sa_row[t][kb];
+#pragma unroll
+                    for (int s = 0; s < kNS; ++s) fw[d][s] = sw_row[s][kb];
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                if (j0 + d < nper) {
+#pragma unroll
+                    for (int s = 0; s < kNS; ++s)
+#pragma unroll
+                        for (int t = 0; t < kMT; ++t) {
+                            if (kBlock) {
+                                const f32x4 p = mma<kFp8>(wf[d][s], af[d][t], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                                const float f = fa[d][t] * fw[d][s];
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) acc[s][t][r] = __builtin_fmaf(p[r], f, acc[s][t][r]);
+                            } else {
+                                acc[s][t] = mma<kFp8>(wf[d][s], af[d][t], acc[s][t]);
+                            }
+                        }
+                }
+            }
+        }
+    }
+
+    if (kKS > 1) {
+        if (wave > 0) {
+#pragma unroll
+            for (int s = 0; s < kNS; ++s)
+#pragma unroll
+                for (int t = 0; t < kMT; ++t) red[wave - 1][s * kMT + t][lane] = acc[s][t];
+        }
+        __syncthreads();
+    }
+    if (wave == 0) {
+        const bool vec_ok = (N & 3) == 0;
+        const QScale q = out_qscale<kOut>(qs);
+#pragma unroll
+        for (int s = 0; s < kNS; ++s)
+#pragma unroll
+            for (int t = 0; t < kMT; ++t) {
+                f32x4 v = acc[s][t];
+#pragma unroll
+                for (int w = 0; w < kKS - 1; ++w) v += red[w][s * kMT + t][lane];
+                const int m = 16 * t + r16;
+                const int64_t n0 = n_base + 16 * s + 4 * (lane >> 4);
+                if (m < M && n0 < N) {
+                    if (kBlock) store4_raw<kOut>(Y, N, m, n0, v, vec_ok, q);
+                    else store4<kOut>(Y, N, m, n0, v, sa[sa_per_token ? m : 0], sw, vec_ok, q);
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers: one 16-row m-tile for M <= 16, two for M <= 32.
+template <bool kFp8, int kOut, bool kWPacked, bool kAPacked, int kMT, int kNS, int kKS, int kDepth>
+static void launch_skinny(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw, void* y,
+                          int M, int N, int K, const float* qs, hipStream_t stream) {
+    dim3 grid((unsigned)((N + 16 * kNS - 1) / (16 * kNS))), block(64 * kKS);
+    gemm_skinny<kFp8, kOut, kMT, kNS, kKS, kDepth, kWPacked, kAPacked>
+        <<<grid, block, 0, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, qs);
+}
+
+template <bool kFp8, int kOut, bool kWPacked, bool kAPacked>
+static hipError_t launch_skinny_t(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw,
+                                  void* y, int M, int N, int K, const float* qs, hipStream_t stream) {
+    if (M <= 16)
+        launch_skinny<kFp8, kOut, kWPacked, kAPacked, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y,
+                                                                                             M, N, K, qs, stream);
+    else
+        launch_skinny<kFp8, kOut, kWPacked, kAPacked, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH>(aq, sa, sa_pt, wq, sw, y,
+                                                                                             M, N, K, qs, stream);
+    return hipGetLastError();
+}
+
+template <bool kFp8, bool kWPacked, bool kAPacked>
+static hipError_t launch_skinny_y(const uint8_t* aq, const float* sa, int pt, const uint8_t* wq, const float* sw,
+                                  void* y, int out_kind, int M, int N, int K, const float* qs, hipStream_t stream) {
+    if (out_kind == kOutBF16)
+        return launch_skinny_t<kFp8, kOutBF16, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, qs, stream);
+    if (out_kind == kOutE4M3)
+        return launch_skinny_t<kFp8, kOutE4M3, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, qs, stream);
+    return launch_skinny_t<kFp8, kOutF32, kWPacked, kAPacked>(aq, sa, pt, wq, sw, y, M, N, K, qs, stream);
+}
+
+template <bool kFp8>
+static hipError_t launch_skinny_m(const uint8_t* aq, bool a_packed, const float* sa, int pt, const uint8_t* wq,
+                                  bool w_packed, const float* sw, void* y, int out_kind, int M, int N, int K,
+                                  const float* qs, hipStream_t stream) {
+    if (a_packed)
+        return w_packed ? launch_skinny_y<kFp8, true, true>(aq, sa, pt, wq, sw, y, out_kind, M, N, K, qs, stream)
+                        : launch_skinny_y<kFp8, false, true>(aq, sa, pt, wq, sw, y, out_kind, M, N, K, qs, stream);
+    return w_packed ? launch_skinny_y<kFp8, true, false>(aq, sa, pt, wq, sw, y, out_kind, M, N, K, qs, stream)
+                    : launch_skinny_y<kFp8, false, false>(aq, sa, pt, wq, sw, y, out_kind, M, N, K, qs, stream);
+}
+
+hipError_t launch_skinny_gemm(const uint8_t* aq, bool a_packed, const float* sa, int sa_per_token, const uint8_t* wq,
+                              bool w_packed, const float* sw, void* y, int out_kind, const float* out_scale, int M,
+                              int N, int K, bool fp8_mfma, hipStream_t stream) {
+    if (fp8_mfma)
+        return launch_skinny_m<true>(aq, a_packed, sa, sa_per_token, wq, w_packed, sw, y, out_kind, M, N, K, out_scale,
+                                     stream);
+    return launch_skinny_m<false>(aq, a_packed, sa, sa_per_token, wq, w_packed, sw, y, out_kind, M, N, K, out_scale,
+                                  stream);
+}
+
+template <bool kFp8, int kOut, bool kWPacked, bool kAPacked>
+static hipError_t launch_skinny_bw_t(const uint8_t* aq, const float* sa, const uint8_t* wq, const float* sw, void* y,
+                                     int M, int N, int K, hipStream_t stream) {
+    dim3 block(64 * SKINNY_KS);
+    dim3 grid((unsigned)((N + 16 * SKINNY_NS - 1) / (16 * SKINNY_NS)));
+    if (M <= 16)
+        gemm_skinny<kFp8, kOut, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
+            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K, nullptr);
+    else
+        gemm_skinny<kFp8, kOut, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
+            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K, nullptr);
+    return hipGetLastError();
+}
+
+template <bool kFp8>
+static hipError_t launch_skinny_bw_m(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq,
+                                     bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
+                                     hipStream_t stream) {
+#define FP8SG_BW(YB, WP, AP) \
+    launch_skinny_bw_t<kFp8, (YB) ? kOutBF16 : kOutF32, WP, AP>(aq, sa, wq, sw, y, M, N, K, stream)
+    if (y_bf16) {
+        if (a_packed) return w_packed ? FP8SG_BW(true, true, true) : FP8SG_BW(true, false, true);
+        return w_packed ? FP8SG_BW(true, true, false) : FP8SG_BW(true, false, false);
+    }
+    if (a_packed) return w_packed ? FP8SG_BW(false, true, true) : FP8SG_BW(false, false, true);
+    return w_packed ? FP8SG_BW(false, true, false) : FP8SG_BW(false, false, false);
+#undef FP8SG_BW
+}
+
+hipError_t launch_skinny_blockwise(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq,
+                                   bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
+                                   bool fp8_mfma, hipStream_t stream) {
+    if (fp8_mfma) return launch_skinny_bw_m<true>(aq, a_packed, sa, wq, w_packed, sw, y, y_bf16, M, N, K, stream);
+    return launch_skinny_bw_m<false>(aq, a_packed, sa, wq, w_packed, sw, y, y_bf16, M, N, K, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode GEMM with the per-token activation quantization fused in (bf16 X,
+// M <= 4, K <= 4096): X [M, K] in, Y out, one launch.
+//
+// The dynamic per-token rule needs each row's maximum before any code, and
+// every workgroup needs all of A, so each workgroup quantizes the few rows
+// itself, while the weight stream is already under way: a wave first issues
+// the loads of its X chunks (one chunk of 8 per thread and row), then the
+// loads of ALL its W blocks (at most kFusedMaxPer, held in registers), and only
+// then waits for X.  Loads complete in issue order, so X arrives first and the
+// quantization (row maxima by wave shuffles and LDS, encode, codes to LDS with
+// rows K + 16 bytes apart) runs while W is in flight.  Rows, chunks and blocks
+// past the valid ones are clamped to valid addresses and masked, so the code
+// between the loads has no branches.  8 waves of at most 128 registers each:
+// the whole weight matrix of the decode shape is then requested at once by
+// workgroups that all fit on the chip together (two per CU).  Workgroup 0
+// also writes the scales for the caller.  The multiplies are the skinny
+// kernel's: W fragments from registers, A fragments from LDS, k blocks split
+// round-robin over the waves, partial sums added in fixed order.
+constexpr int kFusedMaxM = 4;      // rows: with more, the X registers push the wave past 128 VGPRs
+constexpr int kFusedKS = 8;         // waves per workgroup
+constexpr int kFusedRowChunks = 1;  // chunks of 8 per thread and row: K <= 8 * 1 * 64 * kFusedKS
+constexpr int kFusedMaxPer = 4;     // W blocks per wave: K <= 128 * 4 * kFusedKS
+
+__device__ __forceinline__ Frag load_frag_lds(const uint8_t* p) {
+    Frag f;
+    f.lo = reinterpret_cast<const uint4*>(p)[0];
+    f.hi = reinterpret_cast<const uint4*>(p)[1];
+    return f;
+}
+
+template <bool kFp8, int kOut, bool kWPacked, int kNS, int kKS, int kM>
+__global__ __launch_bounds__(64 * kKS) __attribute__((amdgpu_waves_per_eu(4))) void gemm_skinny_fused(
+    const uint16_t* __restrict__ X, float* __restrict__ sa_out, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, const float* __restrict__ qs) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];  // [M][K + 16] codes
+    __shared__ f32x4 red[kKS > 1 ? kKS - 1 : 1][kNS][64];
+    __shared__ float row_max[kKS][kFusedMaxM];
+    __shared__ float row_scale[kFusedMaxM];
+    constexpr int T = 64 * kKS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * kNS);
+    const int nkb = K >> 7;
+    const int r16 = lane & 15, kofs = (lane >> 4) * 32;
+    const int pitch = K + 16;
+    const int row_chunks = K >> 3;
+
+    // 1. X: this thread's chunks of every row (clamped to valid rows / chunks)
+    uint4 xr[kM][kFusedRowChunks];
+#pragma unroll
+    for (int r = 0; r < kM; ++r) {
+        const int rr = r < M ? r : M - 1;
+#pragma unroll
+        for (int i = 0; i < kFusedRowChunks; ++i) {
+            int c = threadIdx.x + i * T;
+            c = c < row_chunks ? c : row_chunks - 1;
+            xr[r][i] = *reinterpret_cast<const uint4*>(X + (int64_t)rr * K + (int64_t)c * 8);
+        }
+    }
+
+    // 2. W: every block of this wave (wave + j * kKS, j < nper; clamped past the end)
+    const int nper = nkb > wave ? (nkb - wave + kKS - 1) / kKS : 0;
+    const uint8_t* wrow[kNS];
+    const int64_t last_tile = ((int64_t)N + 15) / 16 - 1;
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+        if (kWPacked) {
+            int64_t t = (n_base >> 4) + s;
+            t = t < last_tile ? t : last_tile;
+            wrow[s] = W + t * nkb * kPackBlock;
+        } else {
+            int64_t n = n_base + 16 * s + r16;
+            n = n < N ? n : N - 1;
+            wrow[s] = W + n * (int64_t)K + kofs;
+        }
+    }
+    Frag wf[kFusedMaxPer][kNS];
+#pragma unroll
+    for (int j = 0; j < kFusedMaxPer; ++j) {
+        int jj = j < nper ? j : nper - 1;
+        jj = jj > 0 ? jj : 0;
+        int kb = wave + jj * kKS;
+        kb = kb < nkb ? kb : nkb - 1;  // a wave without blocks (nper == 0) loads block nkb - 1, unused
+#pragma unroll
+        for (int s = 0; s < kNS; ++s)
+            wf[j][s] = kWPacked ? load_frag_packed_stream(wrow[s] + kb * kPackBlock, lane)
+                                : load_frag_global(wrow[s] + ((int64_t)kb << 7));
+    }
+
+    // 3. row maxima and scales
+#pragma unroll
+    for (int r = 0; r < kM; ++r) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kFusedRowChunks; ++i) {
+            const uint4 u = xr[r][i];
+            const float a = fmaxf(fmaxf(fmaxf(__builtin_fabsf(bf16_lo(u.x)), __builtin_fabsf(bf16_hi(u.x))),
+                                        fmaxf(__builtin_fabsf(bf16_lo(u.y)), __builtin_fabsf(bf16_hi(u.y)))),
+                                  fmaxf(fmaxf(__builtin_fabsf(bf16_lo(u.z)), __builtin_fabsf(bf16_hi(u.z))),
+                                        fmaxf(__builtin_fabsf(bf16_lo(u.w)), __builtin_fabsf(bf16_hi(u.w)))));
+            const bool valid = (int)threadIdx.x + i * T < row_chunks;
+            amax = valid ? fmaxf(amax, a) : amax;
+        }
+        amax = wave_max(amax);
+        if (lane == 0) row_max[wave][r] = amax;
+    }
+    __syncthreads();
+    if (threadIdx.x < kM) {
+        float m = row_max[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < kKS; ++w) m = fmaxf(m, row_max[w][threadIdx.x]);
+        const float sc = dynamic_scale(m, kE4M3Max);
+        row_scale[threadIdx.x] = sc;
+        if (blockIdx.x == 0 && sa_out != nullptr && (int)threadIdx.x < M) sa_out[threadIdx.x] = sc;
+    }
+    __syncthreads();
+
+    // 4. codes to LDS
+#pragma unroll
+    for (int r = 0; r < kM; ++r) {
+        if (r < M) {
+            const QScale p = make_qscale(row_scale[r], kE4M3Max);
+#pragma unroll
+            for (int i = 0; i < kFusedRowChunks; ++i) {
+                const int c = threadIdx.x + i * T;
+                if (c < row_chunks) {
+                    float v[8];
+                    const uint4 u = xr[r][i];
+                    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+                    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+                    *reinterpret_cast<uint2*>(a_lds + r * pitch + c * 8) = encode_chunk_dynamic<uint16_t>(v, p);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // 5. the multiplies of this wave's blocks
+    f32x4 acc[kNS];
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t* arow = a_lds + (r16 < M ? r16 : M - 1) * pitch + kofs;
+#pragma unroll
+    for (int j = 0; j < kFusedMaxPer; ++j) {
+        if (j < nper) {
+            const Frag af = load_frag_lds(arow + (wave + j * kKS) * 128);
+#pragma unroll
+            for (int s = 0; s < kNS; ++s) acc[s] = mma<kFp8>(wf[j][s], af, acc[s]);
+        }
+    }
+
+    if (kKS > 1) {
+        if (wave > 0) {
+#pragma unroll
+            for (int s = 0; s < kNS; ++s) red[wave - 1][s][lane] = acc[s];
+        }
+        __syncthreads();
+    }
+    if (wave == 0) {
+        const bool vec_ok = (N & 3) == 0;
+        const QScale q = out_qscale<kOut>(qs);
+        const int m = r16;
+#pragma unroll
+        for (int s = 0; s < kNS; ++s) {
+            f32x4 a = acc[s];
+#pragma unroll
+            for (int w = 0; w < kKS - 1; ++w) a += red[w][s][lane];
+            const int64_t n0 = n_base + 16 * s + 4 * (lane >> 4);
+            if (m < M && n0 < N) store4<kOut>(Y, N, m, n0, a, row_scale[m], sw, vec_ok, q);
+        }
+    }
+}
+
+template <bool kFp8, int kOut, bool kWPacked>
+static void launch_fused_t(const uint16_t* x, float* sa_out, const uint8_t* wq, const float* sw, void* y, int M,
+                           int N, int K, const float* qs, hipStream_t stream) {
+    dim3 grid((unsigned)((N + 16 * SKINNY_NS - 1) / (16 * SKINNY_NS))), block(64 * kFusedKS);
+    const size_t lds = (size_t)M * (size_t)(K + 16);
+#define FP8SG_FUSED_M(KM) \
+    gemm_skinny_fused<kFp8, kOut, kWPacked, SKINNY_NS, kFusedKS, KM><<<grid, block, lds, stream>>>(x, sa_out, wq, sw, \
+                                                                                                y, M, N, K, qs)
+    if (M <= 1) FP8SG_FUSED_M(1);
+    else if (M <= 2) FP8SG_FUSED_M(2);
+    else FP8SG_FUSED_M(4);
+#undef FP8SG_FUSED_M
+}
+
+template <bool kFp8, int kOut>
+static void launch_fused_w(const uint16_t* x, float* sa_out, const uint8_t* wq, bool w_packed, const float* sw,
+                           void* y, int M, int N, int K, const float* qs, hipStream_t stream) {
+    if (w_packed) launch_fused_t<kFp8, kOut, true>(x, sa_out, wq, sw, y, M, N, K, qs, stream);
+    else launch_fused_t<kFp8, kOut, false>(x, sa_out, wq, sw, y, M, N, K, qs, stream);
+}
+
+bool gemm_fused_quant_fits(bool x_is_bf16, int64_t M, int64_t K) {
+    return x_is_bf16 && M >= 1 && M <= kFusedMaxM && K <= (int64_t)8 * kFusedRowChunks * 64 * kFusedKS &&
+           K <= (int64_t)128 * kFusedMaxPer * kFusedKS;
+}
+
+hipError_t launch_gemm_fused_quant(const uint16_t* x, float* sa_out, const uint8_t* wq, bool w_packed,
+                                   const float* w_scales, void* y, int out_kind, const float* out_scale, int64_t M,
+                                   int64_t N, int64_t K, bool fp8_mfma, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    const int m = (int)M, n = (int)N, k = (int)K;
+#define FP8SG_FUSED(F8, OUT) launch_fused_w<F8, OUT>(x, sa_out, wq, w_packed, w_scales, y, m, n, k, out_scale, stream)
+    if (fp8_mfma) {
+        if (out_kind == kOutBF16) FP8SG_FUSED(true, kOutBF16);
+        else if (out_kind == kOutE4M3) FP8SG_FUSED(true, kOutE4M3);
+        else FP8SG_FUSED(true, kOutF32);
+    } else {
+        if (out_kind == kOutBF16) FP8SG_FUSED(false, kOutBF16);
+        else if (out_kind == kOutE4M3) FP8SG_FUSED(false, kOutE4M3);
+        else FP8SG_FUSED(false, kOutF32);
+    }
+#undef FP8SG_FUSED
+    return hipGetLastError();
+}
+
+}  // namespace fp8sg
