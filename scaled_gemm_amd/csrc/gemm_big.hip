@@ -414,6 +414,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
 #pragma unroll
         for (int j = 0; j < 4; ++j) f[j] = ls[64 * wm + 16 * j + (lane & 15)] * swv;
         Frag af[4], wf[2];
+        f32x4 p[2][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) af[j] = load_frag_packed(cur + (4 * wm + j) * kPackBlock, lane);
         const uint8_t* lw = cur + (16 + 8 * wn) * kPackBlock;
@@ -430,14 +431,26 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
                 for (int c = 0; c < kBwCopies; ++c) issue_copy(c, cur_lds, nxt);
             }
             __builtin_amdgcn_sched_barrier(0);
+            // the products of W fragment i, then the scaled adds of fragment i - 1, whose
+            // products were issued a row earlier: no add waits for its multiply
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 p = mma_fp8(wf[i & 1], af[j], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            for (int j = 0; j < 4; ++j) p[i & 1][j] = mma_fp8(wf[i & 1], af[j], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            if (i > 0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], f[j], acc[i][j][r]);
+                for (int j = 0; j < 4; ++j) {
+                    f32x4 q = p[(i - 1) & 1][j];
+                    asm volatile("" : "+v"(q));  // keeps the adds in this row (plain arithmetic would be
+                                                 // placed right behind its multiply, which then stalls)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = __builtin_fmaf(q[r], f[j], acc[i - 1][j][r]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[7][j][r] = __builtin_fmaf(p[1][j][r], f[j], acc[7][j][r]);
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
 
