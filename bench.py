@@ -261,6 +261,39 @@ def _tflops(flops, ms):
     return round(flops / (ms * 1e-3) / 1e12, 1)
 
 
+def sustained_clock_mhz(torch, launch, launch_ms, seconds=2.5, settle=0.6, samples=4, gap=0.25):
+    """Graphics clock while the GPU runs back-to-back launches of one kernel.
+
+    Queues about `seconds` of launches, waits `settle` s (the tool's reading
+    trails the load by up to half a second), then reads `amd-smi metric --clock`
+    `samples` times from a child process and averages the 8 XCD clocks of each
+    reading.  Returns (readings or None when the tool is missing or prints no
+    clock, average ms per launch of the loop from HIP events around it)."""
+    import re
+    import shutil
+    import subprocess
+    import time
+    tool = shutil.which("amd-smi")
+    torch.cuda.synchronize()
+    n = max(1, int(seconds * 1e3 / launch_ms))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        launch(i)
+    b.record()
+    vals = []
+    if tool is not None:
+        time.sleep(settle)
+        for _ in range(samples):
+            r = subprocess.run([tool, "metric", "--clock"], capture_output=True, text=True, timeout=30)
+            c = [int(v) for v in re.findall(r"GFX_\d+:\s+CLK: (\d+) MHz", r.stdout)]
+            if c:
+                vals.append(round(sum(c) / len(c)))
+            time.sleep(gap)
+    torch.cuda.synchronize()
+    return (vals or None), a.elapsed_time(b) / n
+
+
 def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
     """Every other configuration: prefill and large-layer GEMMs (both accumulation
     modes), per-token / static / per-channel quantizers and the KV-cache passes."""
@@ -345,8 +378,27 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
                 del qn, sn
             if "prefill" in wanted:
                 wq, sw = sg.fp8_quant_weight_per_channel(torch.from_numpy(w).to(dev))
-                gemm_rows(f"prefill K={K}", xl, wq, sw, M, N, K)
-                del wq, sw
+                aq, sa = gemm_rows(f"prefill K={K}", xl, wq, sw, M, N, K)
+                if K == 14336:
+                    # the clock the matrix cores actually ran at during a long loop of each mode
+                    wp = sg.fp8_pack_weights(wq)
+                    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                    for accum in ("mfma_fp8", "exact"):
+                        f = lambda i: sg.fp8_scaled_gemm(aq, sa, wp, sw, y=y, accum=accum, w_layout="packed")
+                        ms = float(timed_events(f, 3, 1, reps=1).mean())
+                        mhz, ms = sustained_clock_mhz(torch, f, ms)
+                        row = {"workload": f"sustained graphics clock, prefill GEMM {M}x{N}x{K} loop (row-major A, "
+                                           "packed W)", "accum": accum, "avg_us": round(ms * 1e3, 1),
+                               "mhz_samples": mhz}
+                        if mhz:
+                            clk = float(np.median(mhz))
+                            peak = FP8_PEAK_TFLOPS if accum == "mfma_fp8" else BF16_PEAK_TFLOPS
+                            row["mhz_median"] = clk
+                            row["frac_of_peak_at_this_clock"] = round(
+                                _tflops(2.0 * M * N * K, ms) / (peak * clk / 2400.0), 4)
+                        out.append(row)
+                    del wp, y
+                del wq, sw, aq, sa
             del xl, x0
             torch.cuda.empty_cache()
 
