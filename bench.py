@@ -532,6 +532,15 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
             out.append({"workload": f"MX decode GEMM M={m} N={N} K={K}", "accum": "scaled mfma",
                         "avg_us": round(float(d.mean()) * 1e3, 2), "GB_s": _gbs(kb, d.mean()),
                         "frac_hbm": round(_gbs(kb, d.mean()) / HBM_PEAK_GBS, 4)})
+            if m > 16:
+                continue
+            # the same call on bf16 X, quantized to MX blocks inside the GEMM kernel (one launch)
+            d = timed_events(lambda i: sg.fp8_scaled_gemm_mx_bf16(x, wps[i % 8], ws, y=y, w_layout="packed",
+                                                                  w_shape=(N, K)), 100, 20)
+            kb = N * K + ws.numel() + 2 * m * K + 2 * m * N
+            out.append({"workload": f"MX decode call M={m} N={N} K={K} (bf16 X, MX quantization inside the GEMM)",
+                        "accum": "scaled mfma", "avg_us": round(float(d.mean()) * 1e3, 2), "GB_s": _gbs(kb, d.mean()),
+                        "frac_hbm": round(_gbs(kb, d.mean()) / HBM_PEAK_GBS, 4)})
         del wps, wp
         torch.cuda.empty_cache()
         # prefill shapes, E4M3 and E5M2 activations

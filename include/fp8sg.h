@@ -378,6 +378,27 @@ fp8sg_status fp8_scaled_gemm_mx(const uint8_t* a_q, const uint8_t* a_scales, int
                                 int64_t K, void* stream);
 
 /*
+ * The MXFP8 decode GEMM on bf16 activations: every 32-element block of each
+ * row of x is quantized inside the GEMM kernel by the rule above (the codes and
+ * scales fp8_quant_mx writes for the same x), in registers, and multiplied as
+ * in fp8_scaled_gemm_mx -- the same products in the same order, so the result
+ * equals fp8_quant_mx followed by fp8_scaled_gemm_mx bit for bit.  One launch,
+ * no quantized copy of x (the pages' point that engines fuse the activation
+ * quantization into the kernels around it: FP8 Inference Explained, in depth --
+ * "Inside a quantized linear layer").
+ *   x         [M, K] bf16 (uint16 bit patterns), row-major
+ *   a_fmt     format of the activation codes: FP8SG_E4M3 or FP8SG_E5M2
+ *   wq, w_scales, y, y_dtype: as for fp8_scaled_gemm_mx
+ *   layout    0 or FP8SG_W_PACKED (the weights' layout)
+ *   K % 128 == 0; 0 <= M <= 16 (decode shapes).  A larger M returns
+ *   FP8SG_E_SHAPE: every workgroup reads all of x, twice the bytes of its
+ *   codes, so there fp8_quant_mx followed by fp8_scaled_gemm_mx is faster.
+ */
+fp8sg_status fp8_scaled_gemm_mx_bf16(const uint16_t* x, int a_fmt, const uint8_t* wq, const uint8_t* w_scales,
+                                     int layout, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                     void* stream);
+
+/*
  * KV-cache calibration: one scale per kv head, s_h = RN32(amax_h / max) over
  * all (b, s, d) of head h, or 1.0 when that is 0 (per-head KV scales require
  * calibration -- Quantization: FP8 inference and KV-cache quantization,

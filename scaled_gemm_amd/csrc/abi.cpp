@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -353,6 +353,25 @@ fp8sg_status fp8_scaled_gemm_mx(const uint8_t* a_q, const uint8_t* a_scales, int
                                           wq, (layout & FP8SG_W_PACKED) != 0, w_scales, y,
                                           y_dtype == FP8SG_BF16 ? fp8sg::kOutBF16 : fp8sg::kOutF32, M, N, K,
                                           (hipStream_t)stream));
+}
+
+fp8sg_status fp8_scaled_gemm_mx_bf16(const uint16_t* x, int a_fmt, const uint8_t* wq, const uint8_t* w_scales,
+                                     int layout, void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32) || !is_fp8(a_fmt)) return FP8SG_E_DTYPE;
+    if ((layout & ~FP8SG_W_PACKED) != 0) return FP8SG_E_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (K % 128 != 0 || M > 16) return FP8SG_E_SHAPE;
+    if (M == 0 || N == 0) return FP8SG_OK;
+    if (!y) return FP8SG_E_NULL;
+    if (K > 0 && (!x || !wq || !w_scales)) return FP8SG_E_NULL;
+    if ((x && !aligned(x, 16)) || (wq && !aligned(wq, 16)) || !aligned(y, 16)) return FP8SG_E_ALIGN;
+    if (w_scales && !aligned(w_scales, 4)) return FP8SG_E_ALIGN;
+    fp8sg_status d = device_ok();
+    if (d != FP8SG_OK) return d;
+    // K == 0 launches too: the kernel reads no operand and writes the empty sums (zeros)
+    return launched(fp8sg::launch_gemm_mx_bf16x(x, a_fmt == FP8SG_E4M3 ? 0 : 1, wq, (layout & FP8SG_W_PACKED) != 0,
+                                                w_scales, y, y_dtype == FP8SG_BF16 ? fp8sg::kOutBF16 : fp8sg::kOutF32,
+                                                M, N, K, (hipStream_t)stream));
 }
 
 fp8sg_status fp8_kv_calibrate(const uint16_t* kv, int64_t B, int64_t S, int64_t H, int64_t D, int fmt,

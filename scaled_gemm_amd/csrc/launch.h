@@ -62,6 +62,11 @@ hipError_t launch_pack_mx_scales(const uint8_t* s, int64_t R, int64_t K, uint8_t
 hipError_t launch_gemm_mx(const uint8_t* aq, bool a_packed, const uint8_t* a_scales, int a_fmt, const uint8_t* wq,
                           bool w_packed, const uint8_t* w_scales, void* y, int out_kind, int64_t M, int64_t N,
                           int64_t K, hipStream_t stream);
+// The same on bf16 activations X [M, K] (M <= 16), quantized to MX blocks of
+// format a_fmt inside the kernel.
+hipError_t launch_gemm_mx_bf16x(const uint16_t* x, int a_fmt, const uint8_t* wq, bool w_packed,
+                                const uint8_t* w_scales, void* y, int out_kind, int64_t M, int64_t N, int64_t K,
+                                hipStream_t stream);
 
 hipError_t launch_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wp, hipStream_t stream);
 

@@ -29,6 +29,8 @@
 // 16 (4 g + j) + l % 16 and 32-k group l / 16.  A 256-row GEMM tile's scales of
 // one k block are then one contiguous kilobyte, and one dword per lane holds
 // the scales of four tiles.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace fp8sg {
@@ -256,6 +258,46 @@ __device__ __forceinline__ void mx_tile_copy_offsets(uint32_t (&o)[8], int64_t b
     }
 }
 
+// One lane's MX fragment of a bf16 activation block, quantized in registers by
+// the rule of mx_quant_packed (the same codes and scale bytes).  p holds the
+// lane's two halves as bf16: p[0..1] are row r's k [16 g, 16 g + 16) of the
+// 128-k block and p[2..3] its k [64 + 16 g, 64 + 16 g + 16) (l = 16 g + r);
+// the 32-k block of each half is shared with lane l ^ 16.  The instruction
+// takes the scale of 32-k block g of row r from lane 16 g + r: blocks 0 and 1
+// are the first halves of lanes r and 32 + r, blocks 2 and 3 their second
+// halves, so one exchange per half brings each lane its byte.
+template <int kFmt>
+__device__ __forceinline__ void mx_quant_frag(const uint4 (&p)[4], int lane, Frag& f, uint32_t& sbyte) {
+    int kx[2];
+    uint4 o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w[8] = {p[2 * h].x, p[2 * h].y, p[2 * h].z, p[2 * h].w,
+                               p[2 * h + 1].x, p[2 * h + 1].y, p[2 * h + 1].z, p[2 * h + 1].w};
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = bf16_lo(w[i]);
+            v[2 * i + 1] = bf16_hi(w[i]);
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        kx[h] = mx_scale_exp<kFmt>(a);
+        const float rr = __uint_as_float((uint32_t)(127 - kx[h]) << 23);
+        o[h].x = pack4<kFmt>(v[0] * rr, v[1] * rr, v[2] * rr, v[3] * rr);
+        o[h].y = pack4<kFmt>(v[4] * rr, v[5] * rr, v[6] * rr, v[7] * rr);
+        o[h].z = pack4<kFmt>(v[8] * rr, v[9] * rr, v[10] * rr, v[11] * rr);
+        o[h].w = pack4<kFmt>(v[12] * rr, v[13] * rr, v[14] * rr, v[15] * rr);
+    }
+    f.lo = o[0];
+    f.hi = o[1];
+    const int g = lane >> 4, src = 32 * (g & 1) + (lane & 15);
+    const int k0 = __shfl(kx[0], src, 64), k1 = __shfl(kx[1], src, 64);
+    sbyte = (uint32_t)((g < 2 ? k0 : k1) + 127);
+}
+
 // Decode shape (M <= 16 kMT): the skinny kernel's organisation -- 32 weight
 // rows (two 16-row subtiles) per workgroup, four waves splitting the k blocks
 // round-robin, weights streamed into registers with the next block's loads in
@@ -263,7 +305,17 @@ __device__ __forceinline__ void mx_tile_copy_offsets(uint32_t (&o)[8], int64_t b
 // order through LDS.  Per k block a wave also reads one scale dword for its
 // two weight subtiles and one for the activation tiles (both in the packed
 // layout: 256 contiguous bytes per wave).
-template <int kAFmt, int kOut, int kMT, bool kWPacked, bool kAPacked>
+//
+// kAFromX: A is bf16 X [M, K] row-major (as unused); each wave quantizes its
+// own fragments of each k block in registers (mx_quant_frag), so no quantized
+// copy of X is written and no separate launch is needed.  The products and
+// their order are those of the pre-quantized kernel, so the two paths give
+// identical results.  Every workgroup reads all of X, twice the bytes of its
+// codes: at M = 8 the call runs at the speed of the GEMM on pre-quantized
+// codes (12.0 vs 11.7 us for N = 14336, K = 4096), at M = 32 (two m-tiles)
+// those re-reads made it 22.8 us against 3 + 13.4 us for the two launches, so
+// the launcher offers one m-tile (M <= 16) only.
+template <int kAFmt, int kOut, int kMT, bool kWPacked, bool kAPacked, bool kAFromX = false>
 __global__ __launch_bounds__(256) void gemm_skinny_mx(const uint8_t* __restrict__ A, const uint32_t* __restrict__ as,
                                                       const uint8_t* __restrict__ W, const uint32_t* __restrict__ ws,
                                                       void* __restrict__ Y, int M, int N, int K) {
@@ -291,7 +343,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_mx(const uint8_t* __restrict_
     const uint8_t* arow[kMT];
 #pragma unroll
     for (int t = 0; t < kMT; ++t) {
-        if (kAPacked) {
+        if (kAFromX) {
+            int m = 16 * t + r16;
+            m = m < M ? m : M - 1;
+            arow[t] = A + ((int64_t)m * K + kofs) * 2;   // bf16 elements
+        } else if (kAPacked) {
             arow[t] = A + (int64_t)t * nkb * kPackBlock;
         } else {
             int m = 16 * t + r16;
@@ -312,7 +368,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_mx(const uint8_t* __restrict_
 #pragma unroll
         for (int t = 0; t < kMT; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto load_block = [&](int j, Frag (&wx)[kNS], Frag (&ax)[kMT], uint32_t& swx, uint32_t& sax) {
+    // the activation operand of one k block: codes (Frag) or, with kAFromX, the
+    // lane's 64 bytes of bf16 X (two 16-element halves)
+    struct XHalves {
+        uint4 p[4];
+    };
+    using AIn = std::conditional_t<kAFromX, XHalves, Frag>;
+    auto load_block = [&](int j, Frag (&wx)[kNS], AIn (&ax)[kMT], uint32_t& swx, uint32_t& sax) {
         const int kb = wave + j * kKS;
         const int64_t off = (int64_t)kb << 7;
 #pragma unroll
@@ -320,25 +382,48 @@ __global__ __launch_bounds__(256) void gemm_skinny_mx(const uint8_t* __restrict_
             wx[s] = kWPacked ? load_frag_packed_stream(wrow[s] + kb * kPackBlock, lane)
                               : load_frag_mx_global(wrow[s] + off);
 #pragma unroll
-        for (int t = 0; t < kMT; ++t)
-            ax[t] = kAPacked ? load_frag_packed(arow[t] + kb * kPackBlock, lane) : load_frag_mx_global(arow[t] + off);
+        for (int t = 0; t < kMT; ++t) {
+            if constexpr (kAFromX) {
+                const uint4* px = reinterpret_cast<const uint4*>(arow[t] + off * 2);
+                ax[t].p[0] = px[0];
+                ax[t].p[1] = px[1];
+                ax[t].p[2] = px[8];   // + 64 elements
+                ax[t].p[3] = px[9];
+            } else {
+                ax[t] = kAPacked ? load_frag_packed(arow[t] + kb * kPackBlock, lane)
+                                 : load_frag_mx_global(arow[t] + off);
+            }
+        }
         swx = wsp[(int64_t)kb * T4w * 64];
-        sax = asp[(int64_t)kb * T4a * 64];
+        sax = kAFromX ? 0u : asp[(int64_t)kb * T4a * 64];
     };
-    auto mul_block = [&](const Frag (&wx)[kNS], const Frag (&ax)[kMT], uint32_t swx, uint32_t sax) {
+    auto mul_block = [&](const Frag (&wx)[kNS], const AIn (&ax)[kMT], uint32_t swx, uint32_t sax) {
+        Frag af[kMT];
+        uint32_t sb[kMT];
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) {
+            if constexpr (kAFromX) {
+                mx_quant_frag<kAFmt>(ax[t].p, lane, af[t], sb[t]);
+            } else {
+                af[t] = ax[t];
+                sb[t] = scale_byte(sax, t);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < kNS; ++s)
 #pragma unroll
             for (int t = 0; t < kMT; ++t)
-                acc[s][t] = mma_mx<kAFmt>(wx[s], ax[t], acc[s][t], scale_byte(swx, wj + s), scale_byte(sax, t));
+                acc[s][t] = mma_mx<kAFmt>(wx[s], af[t], acc[s][t], scale_byte(swx, wj + s), sb[t]);
     };
     const int nper = nkb > wave ? (nkb - wave + kKS - 1) / kKS : 0;
     if (nper > 0) {
-        Frag wf[kNS], af[kMT];
+        Frag wf[kNS];
+        AIn af[kMT];
         uint32_t swf, saf;
         load_block(0, wf, af, swf, saf);
         for (int j = 0; j + 1 < nper; ++j) {
-            Frag wn[kNS], an[kMT];
+            Frag wn[kNS];
+            AIn an[kMT];
             uint32_t swn, san;
             load_block(j + 1, wn, an, swn, san);
             __builtin_amdgcn_sched_barrier(0);
@@ -541,6 +626,35 @@ static void launch_mx_l(const uint8_t* aq, bool a_packed, const uint8_t* as, con
         if (w_packed) launch_mx_t<kAFmt, kOut, true, false>(aq, as, wq, ws, y, M, N, K, stream);
         else launch_mx_t<kAFmt, kOut, false, false>(aq, as, wq, ws, y, M, N, K, stream);
     }
+}
+
+template <int kAFmt, int kOut, bool kWPacked>
+static void launch_mx_x_t(const uint16_t* x, const uint8_t* wq, const uint8_t* ws, void* y, int M, int N, int K,
+                          hipStream_t stream) {
+    dim3 grid((unsigned)((N + 31) / 32)), block(256);
+    const uint8_t* xa = reinterpret_cast<const uint8_t*>(x);
+    gemm_skinny_mx<kAFmt, kOut, 1, kWPacked, false, true><<<grid, block, 0, stream>>>(
+        xa, nullptr, wq, (const uint32_t*)ws, y, M, N, K);
+}
+
+hipError_t launch_gemm_mx_bf16x(const uint16_t* x, int a_fmt, const uint8_t* wq, bool w_packed,
+                                const uint8_t* w_scales, void* y, int out_kind, int64_t M, int64_t N, int64_t K,
+                                hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (M > 16) return hipErrorInvalidValue;  // one 16-row m-tile only (checked by the ABI)
+    const int m = (int)M, n = (int)N, k = (int)K;
+#define FP8SG_MXX(F, O)                                                            \
+    (w_packed ? launch_mx_x_t<F, O, true>(x, wq, w_scales, y, m, n, k, stream)     \
+              : launch_mx_x_t<F, O, false>(x, wq, w_scales, y, m, n, k, stream))
+    if (a_fmt == 0) {
+        if (out_kind == kOutBF16) FP8SG_MXX(0, kOutBF16);
+        else FP8SG_MXX(0, kOutF32);
+    } else {
+        if (out_kind == kOutBF16) FP8SG_MXX(1, kOutBF16);
+        else FP8SG_MXX(1, kOutF32);
+    }
+#undef FP8SG_MXX
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_mx(const uint8_t* aq, bool a_packed, const uint8_t* a_scales, int a_fmt, const uint8_t* wq,

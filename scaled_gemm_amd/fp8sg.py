@@ -67,6 +67,7 @@ _SIGS = {
     "fp8_quant_mx": (_i32, [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _i32, _vp]),
     "fp8_pack_mx_scales": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_mx": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp]),
+    "fp8_scaled_gemm_mx_bf16": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp]),
     "fp8_kv_decode_attention_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "fp8_kv_decode_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _i64,
                                        ctypes.c_float, _vp, _i32, _vp, _sz, _vp]),
@@ -430,6 +431,32 @@ def fp8_scaled_gemm_mx(a: torch.Tensor, a_scales: torch.Tensor, wq: torch.Tensor
     layout = (W_PACKED if w_packed else 0) | (A_PACKED if a_packed else 0)
     _check(lib().fp8_scaled_gemm_mx(_ptr(a), _ptr(a_scales), _FMT[a_fmt], _ptr(wq), _ptr(w_scales), layout, _ptr(y),
                                     y_code, M, N, K, _stream(stream)), "fp8_scaled_gemm_mx")
+    return y
+
+
+def fp8_scaled_gemm_mx_bf16(x: torch.Tensor, wq: torch.Tensor, w_scales: torch.Tensor, *, a_fmt="e4m3",
+                            out_dtype=torch.bfloat16, w_layout="row_major", w_shape: Optional[tuple] = None,
+                            y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The MX decode GEMM on bf16 x [M, K] (M <= 16): each 32-element block of x
+    is quantized to format a_fmt inside the kernel (the codes and scales of
+    fp8_quant_mx), then multiplied as fp8_scaled_gemm_mx does."""
+    _need(x, "x", (torch.bfloat16,))
+    _need(wq, "wq", (torch.uint8,))
+    if x.dim() != 2:
+        raise ValueError(f"x must be [M, K], got {tuple(x.shape)}")
+    M, K = x.shape
+    w_packed = _LAYOUT[w_layout] == W_PACKED
+    N = int(w_shape[0]) if w_packed else wq.shape[0]
+    if w_packed and (w_shape is None or int(w_shape[1]) != K or wq.numel() != fp8_packed_weight_bytes(N, K)):
+        raise ValueError("w_layout='packed' takes w_shape=(N, K) and fp8_packed_weight_bytes(N, K) bytes")
+    if not w_packed and wq.shape[1] != K:
+        raise ValueError(f"wq has shape {tuple(wq.shape)}, expected K = {K}")
+    _need(w_scales, "w_scales", (torch.uint8,), (fp8_mx_packed_scale_bytes(N, K),))
+    y_code = {torch.bfloat16: BF16, torch.float32: F32}[out_dtype]
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device) if y is None else y
+    _need(y, "y", (out_dtype,), (M, N))
+    _check(lib().fp8_scaled_gemm_mx_bf16(_ptr(x), _FMT[a_fmt], _ptr(wq), _ptr(w_scales), W_PACKED if w_packed else 0,
+                                         _ptr(y), y_code, M, N, K, _stream(stream)), "fp8_scaled_gemm_mx_bf16")
     return y
 
 

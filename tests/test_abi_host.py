@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     names = sg.declared_symbols()
-    assert len(names) == 24
+    assert len(names) == 25
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
     missing = [n for n in names if n not in exported]
@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert sg.lib().fp8sg_version() == 7
+    assert sg.lib().fp8sg_version() == 8
     for st in range(8):
         assert sg.status_string(st)
     assert sg.status_string(99) == "unknown status"
@@ -290,6 +290,19 @@ def test_mx_validation(lib):
     assert lib.fp8_scaled_gemm_mx(A + 8, A, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_ALIGN
     assert lib.fp8_scaled_gemm_mx(A, A + 2, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_ALIGN
     assert lib.fp8_scaled_gemm_mx(None, None, b.E5M2, None, None, 0, None, b.F32, 0, 8, 128, None) == b.OK
+    # GEMM on bf16 activations quantized inside the kernel: as above, plus M <= 16 and W-only layout bits
+    g = lib.fp8_scaled_gemm_mx_bf16
+    assert g(A, b.E4M3, A, A, 0, A, b.E4M3, 4, 8, 128, None) == b.E_DTYPE          # output dtype
+    assert g(A, b.BF16, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_DTYPE          # activation format
+    assert g(A, b.E4M3, A, A, b.A_PACKED, A, b.BF16, 4, 8, 128, None) == b.E_DTYPE  # x is row-major bf16
+    assert g(A, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 96, None) == b.E_SHAPE
+    assert g(A, b.E4M3, A, A, 0, A, b.BF16, 17, 8, 128, None) == b.E_SHAPE         # one 16-row m-tile only
+    assert g(None, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_NULL
+    assert g(A, b.E4M3, A, None, 0, A, b.BF16, 4, 8, 128, None) == b.E_NULL
+    assert g(A, b.E4M3, A, A, 0, None, b.BF16, 4, 8, 128, None) == b.E_NULL
+    assert g(A + 8, b.E4M3, A, A, 0, A, b.BF16, 4, 8, 128, None) == b.E_ALIGN
+    assert g(A, b.E4M3, A, A + 2, 0, A, b.BF16, 4, 8, 128, None) == b.E_ALIGN
+    assert g(None, b.E5M2, None, None, 0, None, b.F32, 0, 8, 128, None) == b.OK
 
 
 def pack_mx_codes_reference(q):

@@ -252,3 +252,77 @@ def test_deterministic_repeats():
     y0 = host(sg.fp8_scaled_gemm_mx(*args, out_dtype=torch.float32))
     for _ in range(3):
         assert np.array_equal(host(sg.fp8_scaled_gemm_mx(*args, out_dtype=torch.float32)), y0)
+
+
+# ---------------------------------------------------------------------------
+# fp8_scaled_gemm_mx_bf16: the decode MX GEMM on bf16 activations quantized inside the kernel.
+
+def _bf16x_cases():
+    rng = np.random.default_rng(21)
+    out = []
+    for m, n, k in ((1, 77, 128), (5, 130, 384), (16, 512, 256), (9, 96, 512), (16, 1000, 1024)):
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        x[:, rng.integers(0, k, 3)] *= 40
+        x[0, :32] = 0.0                               # a zero block
+        if m > 1:
+            x[1, 32:64] *= np.float32(2.0 ** -120)    # a block of tiny values
+        w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        w[rng.integers(0, n, 2), :64] *= 300.0
+        out.append((bf16_bits_from_f32(x), w))
+    return out
+
+
+@pytest.mark.parametrize("a_fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("w_layout", ["row_major", "packed"])
+def test_bf16x_equals_quantize_then_gemm(a_fmt, w_layout):
+    """One launch on bf16 X gives the same bits as fp8_quant_mx followed by
+    fp8_scaled_gemm_mx: the same codes, scales and products in the same order."""
+    for xb, w in _bf16x_cases():
+        M, K = xb.shape
+        N = w.shape[0]
+        x = dev_bf16(xb)
+        wq, ws = sg.fp8_quant_mx(dev(w), "e4m3", layout=w_layout, scale_layout="packed")
+        q, s = sg.fp8_quant_mx(x, a_fmt, layout="packed", scale_layout="packed")
+        kw = dict(a_fmt=a_fmt, w_layout=w_layout, w_shape=(N, K))
+        for out in (torch.float32, torch.bfloat16):
+            y2 = sg.fp8_scaled_gemm_mx(q, s, wq, ws, out_dtype=out, a_layout="packed", a_shape=(M, K), **kw)
+            y1 = sg.fp8_scaled_gemm_mx_bf16(x, wq, ws, out_dtype=out, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(y1.view(torch.int16 if out == torch.bfloat16 else torch.int32),
+                               y2.view(torch.int16 if out == torch.bfloat16 else torch.int32)), \
+                f"{M}x{N}x{K} {a_fmt} {w_layout} {out}"
+
+
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_bf16x_decode_against_the_oracle(m):
+    """Full decode shape, sampled columns: within the scaled matrix cores' bound
+    of the exact sum over the oracle's MX codes of the same bf16 X."""
+    xb, w, _ = decode_inputs(m)
+    wq, we = _quant_w(w)
+    w_in, ws_p = sg.fp8_quant_mx(dev(w), "e4m3", layout="packed", scale_layout="packed")
+    y = sg.fp8_scaled_gemm_mx_bf16(dev_bf16(xb), w_in, ws_p, out_dtype=torch.float32, w_layout="packed",
+                                   w_shape=(14336, 4096))
+    torch.cuda.synchronize()
+    aq, ae = mx.quant_mx(f32_from_bf16_bits(xb), E4M3)
+    cols = np.unique(np.concatenate([np.arange(32), np.arange(0, 14336, 37), np.arange(14336 - 32, 14336)]))
+    exact = mx.gemm_mx_exact(aq, ae, wq[cols], we[cols])
+    bound = mx_bound(mx.dequant_mx(aq, ae), mx.dequant_mx(wq[cols], we[cols]))
+    err = np.abs(host(y)[:, cols].astype(np.float64) - exact)
+    assert (err <= bound).all(), f"M={m}: worst err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
+
+
+def test_bf16x_zero_depth_and_shape_limit():
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    e = torch.zeros((0,), dtype=torch.uint8, device="cuda")
+    y = torch.full((3, 5), 7.0, dtype=torch.float32, device="cuda")
+    lib = sg.lib()
+    st = lib.fp8_scaled_gemm_mx_bf16(x.data_ptr(), sg.E4M3, w.data_ptr(), e.data_ptr(), 0, y.data_ptr(), sg.F32,
+                                     3, 5, 0, None)
+    torch.cuda.synchronize()
+    assert st == 0 and (host(y) == 0).all()
+    xb = torch.zeros((17, 128), dtype=torch.bfloat16, device="cuda")
+    wq = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((sg.fp8_mx_packed_scale_bytes(8, 128),), dtype=torch.uint8, device="cuda")
+    with pytest.raises(RuntimeError):
+        sg.fp8_scaled_gemm_mx_bf16(xb, wq, ws)
