@@ -11,6 +11,10 @@
  *   work is enqueued asynchronously on it; results are visible after the caller
  *   synchronises the stream.  Scales live in device memory, so calls do not
  *   synchronise with the host.
+ * - A call only launches kernels on `stream`: no allocation, no memset, no
+ *   host synchronisation, no other stream.  Sequences of calls can therefore be
+ *   captured into a HIP graph and replayed (the first call on a device queries
+ *   its properties once; make it before capturing).
  * - Tensors are dense and row-major (last extent contiguous).  Data pointers
  *   must be 16-byte aligned; scale pointers 4-byte aligned.
  * - FP8 data travels as raw bytes (uint8): E4M3 is the OCP "fn" variant
