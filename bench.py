@@ -298,13 +298,18 @@ def sustained_clock_mhz(torch, launch, launch_ms, seconds=2.5, settle=0.6, sampl
     Queues about `seconds` of launches, waits `settle` s (the tool's reading
     trails the load by up to half a second), then reads `amd-smi metric --clock`
     `samples` times from a child process and averages the 8 XCD clocks of each
-    reading.  Returns (readings or None when the tool is missing or prints no
-    clock, average ms per launch of the loop from HIP events around it)."""
+    reading.  Returns (readings or None when the tool is missing, prints no
+    clock or the run is under a profiler, average ms per launch of the loop from
+    HIP events around it)."""
     import re
     import shutil
     import subprocess
     import time
     tool = shutil.which("amd-smi")
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        # under rocprofv3 a child process starts with the profiler's library loaded, which
+        # initialises the GPU before the tool's own interpreter starts: no child then
+        tool = None
     torch.cuda.synchronize()
     n = max(1, int(seconds * 1e3 / launch_ms))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
