@@ -195,6 +195,7 @@ def main():
         details.append({"workload": f"decode call M={m} (fused per-token quant + GEMM)", "accum": "exact",
                         "w_layout": "packed", "avg_us": round(float(d.mean()) * 1e3, 2),
                         "GB_s": round(bytes_per_call[m] / (d.mean() * 1e-3) / 1e9, 1)})
+        details += library_rows(torch, timed_events, "decode GEMM", aq, sa, wrm, sw, m, DEC_N, DEC_K, 100, 20)
     kb32, dur32 = kern[(32, "exact", "packed", "packed")]
     achieved = kb32 / (dur32 * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -330,6 +331,31 @@ def sustained_clock_mhz(torch, launch, launch_ms, seconds=2.5, settle=0.6, sampl
     return (vals or None), a.elapsed_time(b) / n
 
 
+def library_rows(torch, timed_events, tag, aq, sa, w_rm, sw, M, N, K, iters, warm):
+    """The same product through the vendor library (torch._scaled_mm, i.e.
+    hipBLASLt), timed beside this library's kernels as a yardstick: row-wise
+    scales (the per-token x per-channel scaling computed here) and unit
+    per-tensor scales (the library's plain FP8 GEMM).  Not part of any path of
+    this library; an error is recorded in the row."""
+    out = []
+    w_rm = w_rm if isinstance(w_rm, list) else [w_rm]
+    a8 = aq.view(torch.float8_e4m3fn)
+    b8 = [w.view(torch.float8_e4m3fn).t() for w in w_rm]  # [K, N] column-major, the operand order it takes
+    one = torch.ones((), dtype=torch.float32, device=aq.device)
+    flops = 2.0 * M * N * K
+    for scaling, s_a, s_b in (("row-wise", sa.view(M, 1), sw.view(1, N)), ("per-tensor (unit)", one, one)):
+        row = {"workload": f"{tag} {M}x{N}x{K} through torch._scaled_mm (hipBLASLt), for comparison",
+               "scaling": scaling}
+        try:
+            d = timed_events(lambda i: torch._scaled_mm(a8, b8[i % len(b8)], scale_a=s_a, scale_b=s_b,
+                                                        out_dtype=torch.bfloat16), iters, warm, reps=3)
+            row.update({"avg_us": round(float(d.mean()) * 1e3, 2), "TFLOPS": _tflops(flops, d.mean())})
+        except Exception as e:  # the library may not offer the scaling on this build
+            row["error"] = str(e).split("\n")[0][:160]
+        out.append(row)
+    return out
+
+
 def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
     """Every other configuration: prefill and large-layer GEMMs (both accumulation
     modes), per-token / static / per-channel quantizers and the KV-cache passes."""
@@ -356,7 +382,7 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
             d = timed_events(lambda i: sg.fp8_scaled_gemm(a_in, sa, wbuf, sw, y=y, accum=accum, w_layout=layout,
                                                           a_layout=a_layout, a_shape=(M, K),
                                                           a_scale_mode="per_token" if static_scale is None
-                                                          else "per_tensor"), 10, 3, reps=3)
+                                                          else "per_tensor"), 10, 10, reps=3)
             tf = _tflops(flops, d.mean())
             row = {"workload": f"{tag} GEMM {M}x{N}x{K} (pre-quantized A)", "accum": accum, "w_layout": layout,
                    "a_layout": a_layout, "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": tf,
@@ -365,12 +391,14 @@ def run_details(sg, torch, dev, to_bf16, timed_events, wanted, log):
                 row["frac_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
             out.append(row)
         del ap
+        if static_scale is None:
+            out.extend(library_rows(torch, timed_events, f"{tag} GEMM", aq, sa, wq_rm, sw, M, N, K, 10, 10))
         ws = torch.empty(sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", M, N, K), dtype=torch.uint8,
                          device=dev)
         mode = "per_token" if static_scale is None else "per_tensor"
         sa_in = None if static_scale is None else sa
         d = timed_events(lambda i: sg.fp8_scaled_gemm(x_list[i % len(x_list)], sa_in, wq, sw, y=y, workspace=ws,
-                                                      a_scale_mode=mode, w_layout="packed"), 10, 3, reps=3)
+                                                      a_scale_mode=mode, w_layout="packed"), 10, 10, reps=3)
         out.append({"workload": f"{tag} call {M}x{N}x{K} (bf16 X, {mode} quant fused)", "accum": "exact",
                     "avg_us": round(float(d.mean()) * 1e3, 1), "TFLOPS": _tflops(flops, d.mean())})
         return aq, sa
