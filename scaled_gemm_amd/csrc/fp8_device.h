@@ -78,6 +78,23 @@ __device__ __forceinline__ float quotient_dynamic(float x, const QScale& p) {
     return __builtin_copysignf(abs_quotient<kTwoCorrections>(__builtin_fabsf(x), p), x);
 }
 
+// abs_quotient with the range test already taken by the caller (kFast ==
+// p.fast), so a loop over many values carries no branch per value.
+template <bool kTwoCorrections, bool kFast>
+__device__ __forceinline__ float abs_quotient_known(float a, const QScale& p) {
+    if (kFast) {
+        float q = a * p.r;
+        float e = __builtin_fmaf(-q, p.s, a);
+        q = __builtin_fmaf(e, p.r, q);
+        if (kTwoCorrections) {
+            e = __builtin_fmaf(-q, p.s, a);
+            q = __builtin_fmaf(e, p.r, q);
+        }
+        return q;
+    }
+    return a / p.s;
+}
+
 // Signed quotient for the given-scale path: |x| is first bounded by
 // c = RN32(fmax s) with a NaN-propagating minimum; every |x| >= c encodes to
 // the maximum code, and the bounded quotient RN32(c / s) lies within a
@@ -87,6 +104,12 @@ template <bool kTwoCorrections>
 __device__ __forceinline__ float quotient_given(float x, const QScale& p) {
     float a = __builtin_elementwise_minimum(__builtin_fabsf(x), p.c);
     return __builtin_copysignf(abs_quotient<kTwoCorrections>(a, p), x);
+}
+
+template <bool kTwoCorrections, bool kFast>
+__device__ __forceinline__ float quotient_given_known(float x, const QScale& p) {
+    float a = __builtin_elementwise_minimum(__builtin_fabsf(x), p.c);
+    return __builtin_copysignf(abs_quotient_known<kTwoCorrections, kFast>(a, p), x);
 }
 
 // Four quotients -> four codes in one dword (byte i = code of t_i).

@@ -2,6 +2,8 @@
 // through LDS by direct global-to-LDS copies, in FP8 mode, exact mode and with
 // block-wise scales.  Operand roles, the k assignment of a lane and the two
 // accumulation modes are described at the top of gemm.hip.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace fp8sg {
@@ -118,20 +120,26 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
             m = m < M ? m : M - 1;
             sam[j] = sa[sa_per_token ? m : 0];
         }
+        auto stage = [&](auto fast_tag) __attribute__((always_inline)) {
+            constexpr bool kFast = decltype(fast_tag)::value;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float s4[4];
-            load_sw4(sw, N, n_base + wn * 128 + 16 * i + 4 * (lane >> 4), s4);
+            for (int i = 0; i < 8; ++i) {
+                float s4[4];
+                load_sw4(sw, N, n_base + wn * 128 + 16 * i + 4 * (lane >> 4), s4);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const f32x4 a = acc[i][j];
-                const int row = 16 * j + (lane & 15), col = 16 * i + 4 * (lane >> 4);
-                const float v0 = (a[0] * sam[j]) * s4[0], v1 = (a[1] * sam[j]) * s4[1];
-                const float v2 = (a[2] * sam[j]) * s4[2], v3 = (a[3] * sam[j]) * s4[3];
-                if (kOut == kOutBF16) epi_put4(wl, row, col, v0, v1, v2, v3);
-                else epi_put4_q(wl, row, col, out_codes4(v0, v1, v2, v3, q));
+                for (int j = 0; j < 8; ++j) {
+                    const f32x4 a = acc[i][j];
+                    const int row = 16 * j + (lane & 15), col = 16 * i + 4 * (lane >> 4);
+                    const float v0 = (a[0] * sam[j]) * s4[0], v1 = (a[1] * sam[j]) * s4[1];
+                    const float v2 = (a[2] * sam[j]) * s4[2], v3 = (a[3] * sam[j]) * s4[3];
+                    if (kOut == kOutBF16) epi_put4(wl, row, col, v0, v1, v2, v3);
+                    else epi_put4_q(wl, row, col, out_codes4_known<kFast>(v0, v1, v2, v3, q));
+                }
             }
-        }
+        };
+        // the output scale's range test once per wave, not once per value
+        if (kOut == kOutE4M3 && !q.fast) stage(std::false_type{});
+        else stage(std::true_type{});
         __syncthreads();
         if (kOut == kOutBF16) epi_store(wl, (uint16_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
         else epi_store_q<128>(wl, (uint8_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
@@ -269,23 +277,29 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
             m = m < M ? m : M - 1;
             sam[j] = sa[sa_per_token ? m : 0];
         }
+        auto stage = [&](auto fast_tag) __attribute__((always_inline)) {
+            constexpr bool kFast = decltype(fast_tag)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = 32 * i + 8 * g + 4 * (lane >> 5);
-                float s4[4];
-                load_sw4(sw, N, n_base + wn * 128 + col, s4);
+                for (int g = 0; g < 4; ++g) {
+                    const int col = 32 * i + 8 * g + 4 * (lane >> 5);
+                    float s4[4];
+                    load_sw4(sw, N, n_base + wn * 128 + col, s4);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x16 a = acc[i][j];
-                    const int row = 32 * j + (lane & 31);
-                    const float v0 = (a[4 * g] * sam[j]) * s4[0], v1 = (a[4 * g + 1] * sam[j]) * s4[1];
-                    const float v2 = (a[4 * g + 2] * sam[j]) * s4[2], v3 = (a[4 * g + 3] * sam[j]) * s4[3];
-                    if (kOut == kOutBF16) epi_put4(wl, row, col, v0, v1, v2, v3);
-                    else epi_put4_q(wl, row, col, out_codes4(v0, v1, v2, v3, q));
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x16 a = acc[i][j];
+                        const int row = 32 * j + (lane & 31);
+                        const float v0 = (a[4 * g] * sam[j]) * s4[0], v1 = (a[4 * g + 1] * sam[j]) * s4[1];
+                        const float v2 = (a[4 * g + 2] * sam[j]) * s4[2], v3 = (a[4 * g + 3] * sam[j]) * s4[3];
+                        if (kOut == kOutBF16) epi_put4(wl, row, col, v0, v1, v2, v3);
+                        else epi_put4_q(wl, row, col, out_codes4_known<kFast>(v0, v1, v2, v3, q));
+                    }
                 }
-            }
+        };
+        // the output scale's range test once per wave, not once per value
+        if (kOut == kOutE4M3 && !q.fast) stage(std::false_type{});
+        else stage(std::true_type{});
         __syncthreads();
         if (kOut == kOutBF16) epi_store(wl, (uint16_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);
         else epi_store_q<128>(wl, (uint8_t*)Y, M, N, m_base + wm * 128, n_base + wn * 128, lane);

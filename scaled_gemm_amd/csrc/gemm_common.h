@@ -104,6 +104,14 @@ __device__ __forceinline__ uint32_t out_codes4(float v0, float v1, float v2, flo
                     quotient_given<true>(v3, q));
 }
 
+// The same with the scale's range test taken once by the caller (kFast ==
+// q.fast): the large-tile epilogues encode 256 values per lane.
+template <bool kFast>
+__device__ __forceinline__ uint32_t out_codes4_known(float v0, float v1, float v2, float v3, const QScale& q) {
+    return pack4<0>(quotient_given_known<true, kFast>(v0, q), quotient_given_known<true, kFast>(v1, q),
+                    quotient_given_known<true, kFast>(v2, q), quotient_given_known<true, kFast>(v3, q));
+}
+
 // Epilogue for one 16x16 fragment: lane holds acc[r] = C[n0 + r][m], r = 0..3.
 // store4 applies the per-token / per-channel scales; store4_raw stores the
 // values as they are (block-wise scales were applied inside the k loop).
