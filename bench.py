@@ -51,8 +51,8 @@ TRAFFIC = {"kernel": "gemm_skinny<false, 1, 2, 2, 4, 1, true, true, false>",
            "sources": ("scaled_gemm_amd/csrc/gemm_skinny.hip", "scaled_gemm_amd/csrc/gemm_common.h",
                        "scaled_gemm_amd/csrc/fp8_device.h"),
            "sha256": ("797e72980ff2a80d55ab2b6d8d479b1ac2618f76b2ac0332abc0c4afae61d362",
-                      "41395d68af2d7059e0ef78463da4775bd83523ac38644413ba143f67d566b4d5",
-                      "dddf2e1dade7862522a15f56f2e066096608bc035e0910256e6699782dff88db"),
+                      "89988b7a08724e97afd6856fd885427340a82060cced107b6d687ad8b1cc68d0",
+                      "0d2b00789594dec510b6f2e4e0550571f66e7a453f59b99894367fce3213d427"),
            "fetch_kib": 29258.0, "write_kib": 896.0,
            "fetch_factor": 1048576.0 / 524299.5, "write_factor": 1048576.0 / 1048576.0}
 DEC_N, DEC_K = 14336, 4096

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fp8sg {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -104,6 +106,11 @@ template <bool kTwoCorrections>
 __device__ __forceinline__ float quotient_given(float x, const QScale& p) {
     float a = __builtin_elementwise_minimum(__builtin_fabsf(x), p.c);
     return __builtin_copysignf(abs_quotient<kTwoCorrections>(a, p), x);
+}
+
+template <bool kTwoCorrections, bool kFast>
+__device__ __forceinline__ float quotient_dynamic_known(float x, const QScale& p) {
+    return __builtin_copysignf(abs_quotient_known<kTwoCorrections, kFast>(__builtin_fabsf(x), p), x);
 }
 
 template <bool kTwoCorrections, bool kFast>
@@ -221,15 +228,21 @@ __device__ __forceinline__ void load_chunk<float>(const float* p, float (&v)[8])
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Eight values -> eight E4M3 codes with the scale's range test taken once for
+// the chunk (the scale is the row's).
 template <typename InT>
 __device__ __forceinline__ uint2 encode_chunk_dynamic(const float (&v)[8], const QScale& p) {
     constexpr bool kTwo = sizeof(InT) == 4;
-    uint2 o;
-    o.x = pack4<0>(quotient_dynamic<kTwo>(v[0], p), quotient_dynamic<kTwo>(v[1], p),
-                   quotient_dynamic<kTwo>(v[2], p), quotient_dynamic<kTwo>(v[3], p));
-    o.y = pack4<0>(quotient_dynamic<kTwo>(v[4], p), quotient_dynamic<kTwo>(v[5], p),
-                   quotient_dynamic<kTwo>(v[6], p), quotient_dynamic<kTwo>(v[7], p));
-    return o;
+    auto enc = [&](auto fast_tag) __attribute__((always_inline)) {
+        constexpr bool kFast = decltype(fast_tag)::value;
+        uint2 o;
+        o.x = pack4<0>(quotient_dynamic_known<kTwo, kFast>(v[0], p), quotient_dynamic_known<kTwo, kFast>(v[1], p),
+                       quotient_dynamic_known<kTwo, kFast>(v[2], p), quotient_dynamic_known<kTwo, kFast>(v[3], p));
+        o.y = pack4<0>(quotient_dynamic_known<kTwo, kFast>(v[4], p), quotient_dynamic_known<kTwo, kFast>(v[5], p),
+                       quotient_dynamic_known<kTwo, kFast>(v[6], p), quotient_dynamic_known<kTwo, kFast>(v[7], p));
+        return o;
+    };
+    return p.fast ? enc(std::true_type{}) : enc(std::false_type{});
 }
 
 }  // namespace fp8sg

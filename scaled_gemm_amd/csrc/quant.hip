@@ -351,16 +351,21 @@ __device__ __forceinline__ uint4 encode16_given(const InT* p, const QScale& sc) 
     float v[8], w[8];
     load_chunk<InT>(p, v);
     load_chunk<InT>(p + 8, w);
-    uint4 o;
-    o.x = pack4<kFmt>(quotient_given<kTwo>(v[0], sc), quotient_given<kTwo>(v[1], sc),
-                      quotient_given<kTwo>(v[2], sc), quotient_given<kTwo>(v[3], sc));
-    o.y = pack4<kFmt>(quotient_given<kTwo>(v[4], sc), quotient_given<kTwo>(v[5], sc),
-                      quotient_given<kTwo>(v[6], sc), quotient_given<kTwo>(v[7], sc));
-    o.z = pack4<kFmt>(quotient_given<kTwo>(w[0], sc), quotient_given<kTwo>(w[1], sc),
-                      quotient_given<kTwo>(w[2], sc), quotient_given<kTwo>(w[3], sc));
-    o.w = pack4<kFmt>(quotient_given<kTwo>(w[4], sc), quotient_given<kTwo>(w[5], sc),
-                      quotient_given<kTwo>(w[6], sc), quotient_given<kTwo>(w[7], sc));
-    return o;
+    // the scale's range test once for the 16 values
+    auto enc = [&](auto fast_tag) __attribute__((always_inline)) {
+        constexpr bool kF = decltype(fast_tag)::value;
+        uint4 o;
+        o.x = pack4<kFmt>(quotient_given_known<kTwo, kF>(v[0], sc), quotient_given_known<kTwo, kF>(v[1], sc),
+                          quotient_given_known<kTwo, kF>(v[2], sc), quotient_given_known<kTwo, kF>(v[3], sc));
+        o.y = pack4<kFmt>(quotient_given_known<kTwo, kF>(v[4], sc), quotient_given_known<kTwo, kF>(v[5], sc),
+                          quotient_given_known<kTwo, kF>(v[6], sc), quotient_given_known<kTwo, kF>(v[7], sc));
+        o.z = pack4<kFmt>(quotient_given_known<kTwo, kF>(w[0], sc), quotient_given_known<kTwo, kF>(w[1], sc),
+                          quotient_given_known<kTwo, kF>(w[2], sc), quotient_given_known<kTwo, kF>(w[3], sc));
+        o.w = pack4<kFmt>(quotient_given_known<kTwo, kF>(w[4], sc), quotient_given_known<kTwo, kF>(w[5], sc),
+                          quotient_given_known<kTwo, kF>(w[6], sc), quotient_given_known<kTwo, kF>(w[7], sc));
+        return o;
+    };
+    return sc.fast ? enc(std::true_type{}) : enc(std::false_type{});
 }
 
 template <typename InT, int kFmt>
