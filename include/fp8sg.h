@@ -201,7 +201,7 @@ size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, 
  *   accum         FP8SG_ACCUM_EXACT or FP8SG_ACCUM_MFMA_FP8
  *   workspace     device buffer of at least fp8_scaled_gemm_workspace_size(...)
  *                 bytes, 256-byte aligned (may be NULL when that size is 0)
- *   K % 128 == 0; M, N >= 0 arbitrary.
+ *   K % 128 == 0 and K < 2^24 (else FP8SG_E_SHAPE); M, N >= 0 arbitrary.
  */
 fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode,
                              const uint8_t* wq, int layout, const float* w_scales, void* y, int y_dtype,
@@ -300,7 +300,7 @@ fp8sg_status fp8_quant_weight_blockwise(const void* w, int w_dtype, int64_t N, i
  *             (with that hardware's in-instruction alignment, see fp8sg_accum);
  *             FP8SG_ACCUM_EXACT: P_g formed exactly on the bf16 matrix cores,
  *             available for M <= 32 only (larger M: FP8SG_E_DTYPE).
- *   K % 128 == 0; M, N >= 0 arbitrary.
+ *   K % 128 == 0 and K < 2^24; M, N >= 0 arbitrary.
  */
 fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales, const uint8_t* wq, int layout,
                                        const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N,
@@ -375,7 +375,7 @@ fp8sg_status fp8_pack_mx_scales(const uint8_t* scales, int64_t rows, int64_t K, 
  *   w_scales  packed E8M0 scales of W (fp8_mx_packed_scale_bytes(N, K) bytes)
  *   y         [M, N] FP8SG_BF16 (round to nearest even) or FP8SG_F32
  *   layout    0 or an OR of FP8SG_W_PACKED and FP8SG_A_PACKED
- *   K % 128 == 0; M, N >= 0 arbitrary.
+ *   K % 128 == 0 and K < 2^24; M, N >= 0 arbitrary.
  */
 fp8sg_status fp8_scaled_gemm_mx(const uint8_t* a_q, const uint8_t* a_scales, int a_fmt, const uint8_t* wq,
                                 const uint8_t* w_scales, int layout, void* y, int y_dtype, int64_t M, int64_t N,
@@ -394,7 +394,7 @@ fp8sg_status fp8_scaled_gemm_mx(const uint8_t* a_q, const uint8_t* a_scales, int
  *   a_fmt     format of the activation codes: FP8SG_E4M3 or FP8SG_E5M2
  *   wq, w_scales, y, y_dtype: as for fp8_scaled_gemm_mx
  *   layout    0 or FP8SG_W_PACKED (the weights' layout)
- *   K % 128 == 0; 0 <= M <= 16 (decode shapes).  A larger M returns
+ *   K % 128 == 0, K < 2^24; 0 <= M <= 16 (decode shapes).  A larger M returns
  *   FP8SG_E_SHAPE: every workgroup reads all of x, twice the bytes of its
  *   codes, so there fp8_quant_mx followed by fp8_scaled_gemm_mx is faster.
  */
@@ -425,17 +425,38 @@ fp8sg_status fp8_kv_quant(const uint16_t* kv, int64_t B, int64_t S, int64_t H, i
                           const float* head_scales, int fmt, uint8_t* out, void* stream);
 
 /*
- * KV-cache dequantization: out = bf16(RN32(dec(code) * s_h)) (round to nearest
- * even).  kvq [B, S, H, D] codes -> out [B, S, H, D] bf16.  D % 16 == 0.
+ * KV-cache dequantization: a stored code reads back as the head's scale times
+ * the code's value (FP8 Inference Explained, in depth -- "Scales and their
+ * granularity": x is approximately s times x_fp8; "FP8 KV cache": backends
+ * that do not compute in FP8 read the cache back and compute in higher
+ * precision; Quantization: FP8 inference and KV-cache quantization -- "Turning
+ * it on in an engine": one scale per attention head).
+ *   kvq          [B, S, H, D] codes of format fmt (FP8SG_E4M3 or FP8SG_E5M2)
+ *   head_scales  [H] fp32, the scales the codes were quantized with
+ *   out          [B, S, H, D] bf16 (output): bf16(RN32(dec(code) * s_h)),
+ *                round to nearest even; a NaN code gives a bf16 NaN
+ *   D % 16 == 0.  The caller owns every buffer; nothing else is written.
  */
 fp8sg_status fp8_kv_dequant(const uint8_t* kvq, int64_t B, int64_t S, int64_t H, int64_t D,
                             const float* head_scales, int fmt, uint16_t* out, void* stream);
 
 /*
- * Append one token per sequence: kv_new [B, H, D] bf16 is quantized with the
- * existing per-head scales (saturating) and written to cache[b, pos[b], :, :]
- * of cache [B, S_cap, H, D]; nothing else is written.  pos [B] int32 (device);
- * a sequence whose pos[b] lies outside [0, S_cap) is skipped.  D % 16 == 0.
+ * Append one token per sequence to an FP8 KV cache.  The new keys or values
+ * are quantized with the head scales the cache already holds: the static
+ * scales of a calibrated cache (Quantization: FP8 inference and KV-cache
+ * quantization -- "Turning it on in an engine": per-head scales come from
+ * calibration), so a new value beyond max * s_h saturates to the format's
+ * maximum ("Dynamic scales or static scales": static scales clip inputs more
+ * extreme than the calibration set; FP8 Inference Explained, in depth -- "FP8
+ * KV cache").
+ *   kv_new       [B, H, D] bf16 (uint16 bit patterns)
+ *   pos          [B] int32 (device): the position each sequence writes; a
+ *                sequence whose pos[b] lies outside [0, S_cap) is skipped
+ *   head_scales  [H] fp32 per-head scales of the cache
+ *   fmt          FP8SG_E4M3 or FP8SG_E5M2
+ *   cache        [B, S_cap, H, D] codes: cache[b, pos[b], h, :] =
+ *                FMT(RN32(kv_new[b, h, :] / s_h)); nothing else is written
+ *   D % 16 == 0.
  */
 fp8sg_status fp8_kv_append(const uint16_t* kv_new, const int32_t* pos, int64_t B, int64_t S_cap,
                            int64_t H, int64_t D, const float* head_scales, int fmt,

@@ -15,6 +15,9 @@ namespace {
 
 constexpr int kAbiVersion = 8;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
+// The GEMM kernels keep per-lane operand offsets within a tile in 32 bits:
+// rows x K bytes of a 256-row tile must stay below 2^32.
+constexpr int64_t kMaxGemmK = (int64_t)1 << 24;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -165,7 +168,7 @@ fp8sg_status scaled_gemm_impl(const void* a, int a_dtype, float* a_scales, int a
     if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
     if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED)) != 0) return FP8SG_E_DTYPE;
     if ((layout & FP8SG_A_PACKED) && a_dtype != FP8SG_E4M3) return FP8SG_E_DTYPE;  // only codes come packed
-    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxGemmK) return FP8SG_E_SHAPE;
     if (K % 128 != 0) return FP8SG_E_SHAPE;
     if (M == 0 || N == 0) return FP8SG_OK;
     if (!y || !w_scales) return FP8SG_E_NULL;
@@ -268,7 +271,7 @@ fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales
     if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
     if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
     if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED)) != 0) return FP8SG_E_DTYPE;
-    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxGemmK) return FP8SG_E_SHAPE;
     if (K % 128 != 0) return FP8SG_E_SHAPE;
     if (accum == FP8SG_ACCUM_EXACT && M > 32) return FP8SG_E_DTYPE;  // exact partials: skinny kernel only
     if (M == 0 || N == 0) return FP8SG_OK;
@@ -339,7 +342,7 @@ fp8sg_status fp8_scaled_gemm_mx(const uint8_t* a_q, const uint8_t* a_scales, int
                                 int64_t K, void* stream) {
     if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32) || !is_fp8(a_fmt)) return FP8SG_E_DTYPE;
     if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED)) != 0) return FP8SG_E_DTYPE;
-    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxGemmK) return FP8SG_E_SHAPE;
     if (K % 128 != 0) return FP8SG_E_SHAPE;
     if (M == 0 || N == 0) return FP8SG_OK;
     if (!y) return FP8SG_E_NULL;
@@ -359,7 +362,7 @@ fp8sg_status fp8_scaled_gemm_mx_bf16(const uint16_t* x, int a_fmt, const uint8_t
                                      int layout, void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32) || !is_fp8(a_fmt)) return FP8SG_E_DTYPE;
     if ((layout & ~FP8SG_W_PACKED) != 0) return FP8SG_E_DTYPE;
-    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8SG_E_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxGemmK) return FP8SG_E_SHAPE;
     if (K % 128 != 0 || M > 16) return FP8SG_E_SHAPE;
     if (M == 0 || N == 0) return FP8SG_OK;
     if (!y) return FP8SG_E_NULL;

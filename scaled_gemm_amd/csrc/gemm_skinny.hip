@@ -503,7 +503,9 @@ static void launch_fused_w(const uint16_t* x, float* sa_out, const uint8_t* wq, 
 }
 
 bool gemm_fused_quant_fits(bool x_is_bf16, int64_t M, int64_t K) {
-    return x_is_bf16 && M >= 1 && M <= kFusedMaxM && K <= (int64_t)8 * kFusedRowChunks * 64 * kFusedKS &&
+    // K >= 128: the fused kernel's loads assume at least one k block (an empty
+    // reduction goes through the row quantizer, which writes the unit scales)
+    return x_is_bf16 && M >= 1 && M <= kFusedMaxM && K >= 128 && K <= (int64_t)8 * kFusedRowChunks * 64 * kFusedKS &&
            K <= (int64_t)128 * kFusedMaxPer * kFusedKS;
 }
 

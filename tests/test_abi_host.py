@@ -163,6 +163,39 @@ def test_gemm_validation(lib):
     assert call(a_dt=b.BF16, mode=b.SCALE_PER_TENSOR, sa=None, ws=A, wsb=need) == b.E_NULL
 
 
+def test_gemm_empty_reduction_takes_the_row_quantizer(lib):
+    # K == 0 never reaches the decode kernel that quantizes inside the GEMM (its
+    # loads assume at least one k block): a bf16 per-token call with K == 0 asks
+    # for the workspace of the two-kernel path (no codes, the unit scales)
+    for m in (1, 4):
+        assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, m, 8, 0) == 256
+        assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, m, 8, 128) == 0
+    g = lib.fp8_scaled_gemm
+    # without that workspace the call is refused before any HIP call
+    assert g(None, b.BF16, None, b.SCALE_PER_TOKEN, None, 0, A, A, b.BF16, 4, 8, 0, b.ACCUM_EXACT, None, 0,
+             None) == b.E_WORKSPACE
+    assert g(None, b.BF16, A, b.SCALE_PER_TOKEN, None, 0, A, A, b.BF16, 1, 8, 0, b.ACCUM_EXACT, None, 0,
+             None) == b.E_WORKSPACE
+
+
+def test_gemm_reduction_length_limit(lib):
+    # per-lane tile offsets are 32-bit: K < 2^24 on every GEMM entry point
+    big = 1 << 24
+    g = lib.fp8_scaled_gemm
+    assert g(A, b.E4M3, A, b.SCALE_PER_TOKEN, A, 0, A, A, b.BF16, 64, 8, big, b.ACCUM_EXACT, None, 0,
+             None) == b.E_SHAPE
+    import torch
+    if not torch.cuda.is_available():  # with a device these fake addresses would reach a kernel
+        assert g(A, b.E4M3, A, b.SCALE_PER_TOKEN, A, 0, A, A, b.BF16, 64, 8, big - 128, b.ACCUM_EXACT, None, 0,
+                 None) == b.E_DEVICE
+    assert lib.fp8_scaled_gemm_fp8out(A, b.E4M3, A, b.SCALE_PER_TOKEN, A, 0, A, A, A, 64, 8, big, b.ACCUM_EXACT,
+                                      None, 0, None) == b.E_SHAPE
+    assert lib.fp8_scaled_gemm_blockwise(A, A, A, 0, A, A, b.BF16, 64, 8, big, b.ACCUM_MFMA_FP8,
+                                         None) == b.E_SHAPE
+    assert lib.fp8_scaled_gemm_mx(A, A, b.E4M3, A, A, 0, A, b.BF16, 64, 8, big, None) == b.E_SHAPE
+    assert lib.fp8_scaled_gemm_mx_bf16(A, b.E4M3, A, A, 0, A, b.BF16, 4, 8, big, None) == b.E_SHAPE
+
+
 def test_pack_validation(lib):
     assert lib.fp8_packed_weight_bytes(17, 256) == 32 * 256
     assert lib.fp8_packed_weight_bytes(0, 256) == 0
