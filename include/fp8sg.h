@@ -55,8 +55,13 @@ typedef enum fp8sg_status {
     FP8SG_E_DTYPE = 4,      /* unsupported dtype / format / mode value                 */
     FP8SG_E_DEVICE = 5,     /* no HIP device, or the current device is not gfx950      */
     FP8SG_E_LAUNCH = 6,     /* a kernel launch failed (hipGetLastError)                */
-    FP8SG_E_WORKSPACE = 7   /* workspace missing or smaller than the size query says   */
+    FP8SG_E_WORKSPACE = 7,  /* workspace missing or smaller than the size query says   */
+    FP8SG_E_SCRATCH = 8     /* fp8_scaled_gemm_noalloc: the call needs more than
+                               FP8SG_SCRATCH_BYTES of scratch                           */
 } fp8sg_status;
+
+/* Bytes of the static device scratch behind fp8_scaled_gemm_noalloc (16 MiB). */
+#define FP8SG_SCRATCH_BYTES (16u << 20)
 
 typedef enum fp8sg_dtype {
     FP8SG_F32 = 0,
@@ -207,6 +212,29 @@ fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_
                              const uint8_t* wq, int layout, const float* w_scales, void* y, int y_dtype,
                              int64_t M, int64_t N, int64_t K, int accum,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_scaled_gemm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels and results as fp8_scaled_gemm with the same arguments, but
+ * the workspace (the activation codes and per-token scales this call computes)
+ * is a static device array of FP8SG_SCRATCH_BYTES inside the library, one
+ * copy per device, held until the process ends.  The call allocates nothing;
+ * the caller still provides a, a_scales, wq, w_scales and y as for
+ * fp8_scaled_gemm.
+ *   Arguments as for fp8_scaled_gemm, without workspace / workspace_bytes.
+ *   A call whose fp8_scaled_gemm_workspace_size(...) exceeds
+ *   FP8SG_SCRATCH_BYTES returns FP8SG_E_SCRATCH, with nothing enqueued (e.g.
+ *   bf16 per-token activations of more than about 16.7 M elements).
+ * Every call on a device shares that device's scratch, and nothing in it has
+ * to start cleared (each call writes what it reads).  Calls that overlap on
+ * one device -- on different streams, or from different threads -- race on
+ * it: serialise them.  The first call on a device looks up the scratch's
+ * device address; make it before capturing a graph.
+ */
+fp8sg_status fp8_scaled_gemm_noalloc(const void* a, int a_dtype, float* a_scales, int a_scale_mode,
+                                     const uint8_t* wq, int layout, const float* w_scales, void* y, int y_dtype,
+                                     int64_t M, int64_t N, int64_t K, int accum, void* stream);
 
 /*
  * Scaled GEMM with an FP8 output epilogue: the result is written as the E4M3

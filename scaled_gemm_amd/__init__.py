@@ -42,6 +42,7 @@ from .fp8sg import (  # noqa: F401
     fp8_scaled_gemm_fp8out,
     fp8_scaled_gemm_mx,
     fp8_scaled_gemm_mx_bf16,
+    fp8_scaled_gemm_noalloc,
     fp8_scaled_gemm_workspace_size,
     lib,
     status_string,

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid / int32 index limit per dimension
 // The GEMM kernels keep per-lane operand offsets within a tile in 32 bits:
 // rows x K bytes of a 256-row tile must stay below 2^32.
@@ -91,6 +91,7 @@ const char* fp8sg_status_string(int status) {
         case FP8SG_E_DEVICE: return "no gfx950 HIP device";
         case FP8SG_E_LAUNCH: return "kernel launch failed";
         case FP8SG_E_WORKSPACE: return "workspace missing or too small";
+        case FP8SG_E_SCRATCH: return "call needs more than the library's static scratch (FP8SG_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -157,12 +158,51 @@ fp8sg_status fp8_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* 
     return launched(fp8sg::launch_pack_weights(wq, N, K, wp, (hipStream_t)stream));
 }
 
-static // fp8_scaled_gemm and fp8_scaled_gemm_fp8out: out_kind fp8sg::kOutF32 / kOutBF16 /
-// kOutE4M3 (then out_scale [1] is the per-tensor output scale).
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Static scratch of fp8_scaled_gemm_noalloc: the activation codes and scales
+// that fp8_scaled_gemm writes to its caller's workspace.  Every device the
+// library runs on holds one copy until the process ends.  In host code the
+// array's name is only a stand-in; the device address of each device's copy
+// is looked up once (hipGetSymbolAddress, with that device current) and only
+// that address is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)FP8SG_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[64];
+
+// Device address of the current device's scratch, or NULL on failure.  Called
+// after device_ok(), so the device index is valid.
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        // the same address for every thread that looks it up, so a race only repeats the lookup
+        g_scratch_ptr[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
+// fp8_scaled_gemm, fp8_scaled_gemm_fp8out and fp8_scaled_gemm_noalloc:
+// out_kind fp8sg::kOutF32 / kOutBF16 / kOutE4M3 (then out_scale [1] is the
+// per-tensor output scale).  use_scratch: the workspace is the static scratch
+// (workspace and workspace_bytes are ignored).
 fp8sg_status scaled_gemm_impl(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
                               int layout, const float* w_scales, void* y, int out_kind, const float* out_scale,
                               int64_t M, int64_t N, int64_t K, int accum, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              void* stream, bool use_scratch = false) {
     if (!(a_dtype == FP8SG_E4M3 || is_hp(a_dtype))) return FP8SG_E_DTYPE;
     if (!(a_scale_mode == FP8SG_SCALE_PER_TOKEN || a_scale_mode == FP8SG_SCALE_PER_TENSOR)) return FP8SG_E_DTYPE;
     if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
@@ -184,12 +224,19 @@ fp8sg_status scaled_gemm_impl(const void* a, int a_dtype, float* a_scales, int a
     if ((a_scales && !aligned(a_scales, 4)) || !aligned(w_scales, 4)) return FP8SG_E_ALIGN;
     if (out_scale && !aligned(out_scale, 4)) return FP8SG_E_ALIGN;
     const size_t need = fp8_scaled_gemm_workspace_size(a_dtype, a_scale_mode, M, N, K);
-    if (need > 0) {
+    if (use_scratch) {
+        if (need > kScratchBytes) return FP8SG_E_SCRATCH;
+    } else if (need > 0) {
         if (!workspace || workspace_bytes < need) return FP8SG_E_WORKSPACE;
         if (!aligned(workspace, 256)) return FP8SG_E_ALIGN;
     }
     fp8sg_status d = device_ok();
     if (d != FP8SG_OK) return d;
+    if (use_scratch) {
+        workspace = need > 0 ? scratch_on_current_device() : nullptr;
+        if (need > 0 && workspace == nullptr) return FP8SG_E_DEVICE;
+        workspace_bytes = need > 0 ? kScratchBytes : 0;
+    }
     hipStream_t s = (hipStream_t)stream;
 
     if (quantize_here && per_token && fp8sg::gemm_fused_quant_fits(a_dtype == FP8SG_BF16, M, K)) {
@@ -219,6 +266,18 @@ fp8sg_status scaled_gemm_impl(const void* a, int a_dtype, float* a_scales, int a
                                        out_kind, out_scale, M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, s));
 }
 
+}  // namespace
+
+extern "C" {
+
+fp8sg_status fp8_scaled_gemm_noalloc(const void* a, int a_dtype, float* a_scales, int a_scale_mode,
+                                     const uint8_t* wq, int layout, const float* w_scales, void* y, int y_dtype,
+                                     int64_t M, int64_t N, int64_t K, int accum, void* stream) {
+    if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
+    return scaled_gemm_impl(a, a_dtype, a_scales, a_scale_mode, wq, layout, w_scales, y,
+                            y_dtype == FP8SG_BF16 ? fp8sg::kOutBF16 : fp8sg::kOutF32, nullptr, M, N, K, accum,
+                            nullptr, 0, stream, true);
+}
 
 fp8sg_status fp8_scaled_gemm(const void* a, int a_dtype, float* a_scales, int a_scale_mode, const uint8_t* wq,
                              int layout, const float* w_scales, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libfp8sg.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8sg.h")
 
 # enums of include/fp8sg.h
-OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_DEVICE, E_LAUNCH, E_WORKSPACE = range(8)
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_DEVICE, E_LAUNCH, E_WORKSPACE, E_SCRATCH = range(9)
+SCRATCH_BYTES = 16 << 20  # FP8SG_SCRATCH_BYTES
 F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
 SCALE_PER_TOKEN, SCALE_PER_TENSOR = 0, 1
 W_ROW_MAJOR, W_PACKED, A_PACKED, MX_SCALES_PACKED = 0, 1, 2, 4
@@ -57,6 +58,8 @@ _SIGS = {
     "fp8_pack_weights": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _sz,
                                _vp]),
+    "fp8_scaled_gemm_noalloc": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32,
+                                       _vp]),
     "fp8_scaled_gemm_fp8out": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp,
                                       _sz, _vp]),
     "fp8_quant_per_token_group": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]),
@@ -219,7 +222,7 @@ def _scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Te
                  a_scale_mode="per_token", out_dtype=torch.bfloat16, accum="exact", w_layout="row_major",
                  a_layout="row_major", a_shape: Optional[tuple] = None, y: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None,
-                 stream=None) -> torch.Tensor:
+                 noalloc: bool = False, stream=None) -> torch.Tensor:
     """Shared body of fp8_scaled_gemm and fp8_scaled_gemm_fp8out (out_scale given)."""
     _need(a, "a", (torch.uint8, torch.bfloat16, torch.float32))
     _need(wq, "wq", (torch.uint8,))
@@ -249,6 +252,11 @@ def _scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Te
     y_code = {torch.bfloat16: BF16, torch.float32: F32, torch.uint8: E4M3}[out_dtype]
     y = torch.empty((M, N), dtype=out_dtype, device=a.device) if y is None else y
     _need(y, "y", (out_dtype,), (M, N))
+    if noalloc:
+        _check(lib().fp8_scaled_gemm_noalloc(_ptr(a), a_code, _ptr(a_scales), mode, _ptr(wq), layout,
+                                             _ptr(w_scales), _ptr(y), y_code, M, N, K, _ACCUM[accum],
+                                             _stream(stream)), "fp8_scaled_gemm_noalloc")
+        return y
     need = int(lib().fp8_scaled_gemm_workspace_size(a_code, mode, M, N, K))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
@@ -263,6 +271,16 @@ def _scaled_gemm(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Te
                                  y_code, M, N, K, _ACCUM[accum], _ptr(workspace), ws_bytes, _stream(stream)),
            "fp8_scaled_gemm")
     return y
+
+
+def fp8_scaled_gemm_noalloc(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor,
+                            w_scales: torch.Tensor, **kw) -> torch.Tensor:
+    """fp8_scaled_gemm with the library's static device scratch in place of a
+    workspace (the C call allocates nothing; pass y to allocate nothing here
+    either).  Keywords as for fp8_scaled_gemm, without workspace."""
+    if "workspace" in kw:
+        raise TypeError("fp8_scaled_gemm_noalloc takes no workspace")
+    return _scaled_gemm(a, a_scales, wq, w_scales, noalloc=True, **kw)
 
 
 def fp8_scaled_gemm_fp8out(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq: torch.Tensor,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     names = sg.declared_symbols()
-    assert len(names) == 25
+    assert len(names) == 26
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
     missing = [n for n in names if n not in exported]
@@ -26,8 +26,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert sg.lib().fp8sg_version() == 8
-    for st in range(8):
+    assert sg.lib().fp8sg_version() == 9
+    for st in range(9):
         assert sg.status_string(st)
     assert sg.status_string(99) == "unknown status"
 
@@ -385,3 +385,22 @@ def test_rmsnorm_quant_validation(lib):
     assert f(A, b.BF16, None, 1e-6, 4, 128, A, A, None, 0, None) == b.E_NULL
     assert f(A, b.BF16, A, 1e-6, 4, 128, A, A, A + 4, 0, None) == b.E_ALIGN
     assert f(None, b.BF16, None, 1e-6, 0, 128, None, None, None, 0, None) == b.OK
+
+
+def test_noalloc_gemm_validation(lib):
+    """fp8_scaled_gemm_noalloc: the fp8_scaled_gemm checks, and a call whose
+    workspace would exceed the static scratch is refused before any HIP call."""
+    g = lib.fp8_scaled_gemm_noalloc
+    cap = b.SCRATCH_BYTES
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4092, 8, 4096) == cap
+    assert g(A, b.BF16, None, b.SCALE_PER_TOKEN, A, 0, A, A, b.BF16, 4093, 8, 4096, b.ACCUM_EXACT,
+             None) == b.E_SCRATCH
+    assert g(A, b.F32, A, b.SCALE_PER_TENSOR, A, 0, A, A, b.BF16, 8193, 8, 2048, b.ACCUM_EXACT,
+             None) == b.E_SCRATCH
+    assert g(A, b.BF16, None, b.SCALE_PER_TOKEN, A, 0, A, A, b.E4M3, 4, 8, 128, b.ACCUM_EXACT, None) == b.E_DTYPE
+    assert g(A, b.BF16, None, b.SCALE_PER_TOKEN, A, 0, A, A, b.BF16, 4, 8, 100, b.ACCUM_EXACT, None) == b.E_SHAPE
+    assert g(A, b.BF16, None, b.SCALE_PER_TOKEN, None, 0, A, A, b.BF16, 4, 8, 128, b.ACCUM_EXACT,
+             None) == b.E_NULL
+    assert g(None, b.BF16, None, b.SCALE_PER_TOKEN, None, 0, A, A, b.BF16, 0, 8, 128, b.ACCUM_EXACT,
+             None) == b.OK
+    assert "scratch" in sg.status_string(b.E_SCRATCH)
