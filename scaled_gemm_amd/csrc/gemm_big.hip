@@ -160,27 +160,51 @@ __global__ __launch_bounds__(256, 1) void gemm_big_fp8(const uint8_t* __restrict
     }
 }
 
-// Exact mode.  The FP8 codes are widened to bf16 (exact) and multiplied by
-// v_mfma_f32_32x32x16_bf16: each wave's 128 x 128 share is 4 x 4 tiles of
-// 32 x 32, 8 steps of 16 k per k block.  Staging and copy schedule as in FP8
-// mode: two stages, copies two blocks ahead, each stage refilled as soon as
-// every wave holds its bytes in registers.
+// Exact mode.  The FP8 codes are widened to bf16 (exact: every E4M3 value is a
+// bf16 value) and multiplied by v_mfma_f32_32x32x16_bf16: each wave's 128 x 128
+// share is 4 x 4 tiles of 32 x 32, with all 256 accumulator registers (one
+// wave per SIMD).  With a single wave per SIMD nothing hides a stall, so the
+// loop is software-pipelined by hand:
+//
+//  * The k range is walked in half blocks of 64 (the two 1 KB halves of each
+//    16-row x 128-k fragment block).  LDS holds a ring of four half-block
+//    slots of 32 KB (A 16 KB, W 16 KB).  The copies of half block h + 4 go
+//    into slot h % 4 while half block h is multiplied, so each copy has three
+//    half blocks (~6000 matrix-core cycles) to arrive.
+//  * One barrier per half block.  Before it a wave waits for its own copies of
+//    half block h + 1 (vmcnt: the copies of h + 2 and h + 3 stay in flight) and
+//    for its own reads of half block h (lgkmcnt(0)); after it every copy of
+//    h + 1 has landed and nobody reads slot h % 4 any more.
+//  * The fragments of half block h + 1 are read from LDS into registers while
+//    half block h is multiplied (two register sets of 64 VGPRs), and each
+//    16-k step widens the operands of the next step between its own 16
+//    multiplies (two sets of 32 VGPRs), so the matrix core never waits for a
+//    read or a convert.
 //
 // Operand lane layout of the 32 x 32 x 16 instruction: lane l supplies row
-// l % 32 and k 8 (l / 32) .. 8 (l / 32) + 7 of the step.  Step s of a k block
-// gives lane l the 8 bytes at offset 8 (s % 4) of the row's 32-byte slice
-// q = 2 (l / 32) + s / 4, i.e. exactly the bytes that lane (l % 16) + 16 q of the
-// row's 16-row subtile holds in the 16 x 16 fragment order of LDS; A and W use
-// the same assignment, so every product pairs matching k.  Output lane layout:
-// acc[r] of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of the tile.
+// l % 32 and k 8 (l / 32) .. 8 (l / 32) + 7 of the step.  Within half block
+// (kb, h) the 16-row subtile's lane slot s = (r % 16) + 16 q holds bytes
+// [32 q + 16 h, 32 q + 16 h + 16) of row r's 128 k; step t (0..3) gives lane l
+// the 8 bytes at offset 8 (t % 2) of slot q = 2 (l / 32) + t / 2 of row l % 32.
+// A and W use the same assignment, so every product pairs matching k, and the
+// 8 steps of a k block cover its 128 k once.  Output lane layout: acc[r] of
+// lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of the tile.
+constexpr int kExSlot = 32 * 1024;   // one half-block slot: A 16 KB + W 16 KB
+constexpr int kExSlots = 4;
+static_assert(4 * kEpiWaveBytes <= kExSlots * kExSlot, "the staged output reuses the slots");
+
+// s_waitcnt immediate for vmcnt(n) and lgkmcnt(0).
+constexpr int wait_vmcnt_lgkm0(int n) {
+    return 0x0070 | (n & 15) | ((n >> 4) << 14);
+}
+
 template <int kOut, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                          int sa_per_token, const uint8_t* __restrict__ W,
                                                          const float* __restrict__ sw, void* __restrict__ Y, int M,
                                                          int N, int K, int tiles_per_xcd,
                                                          const float* __restrict__ qs) {
-    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages x (A 32 KB + W 32 KB)
-    constexpr int kStage = 32 * kPackBlock;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // kExSlots x kExSlot
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave & 1, wn = wave >> 1;
@@ -189,6 +213,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
     tile_coords(M, N, tiles_per_xcd, tile, m_base, n_base);
     if (tile < 0) return;
     const int nkb = K >> 7;
+    const int nhb = 2 * nkb;   // half blocks
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -198,76 +223,127 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    uint32_t oa[8], ow[8];
-    tile_copy_offsets<kAPacked>(oa, m_base, M, K, wave, lane);
-    tile_copy_offsets<kWPacked>(ow, n_base, N, K, wave, lane);
-    const uint8_t* a_tile = kAPacked ? A + (m_base >> 4) * (int64_t)nkb * kPackBlock : A + m_base * K;
-    const uint8_t* w_tile = kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K;
-    const int64_t a_kb = kAPacked ? kPackBlock : 128;
-    const int64_t w_kb = kWPacked ? kPackBlock : 128;
-
-    // Byte offset of this lane's first 16-byte half of slice q = 2 (lane / 32)
-    // within a 32-row tile: subtile (lane % 32) / 16, row lane % 16.
-    const int lane_off = ((lane & 31) >> 4) * (int)kPackBlock + (lane & 15) * 16 + (lane >> 5) * 512;
-
-    if (nkb > 0) {
-        const int b1 = nkb > 1 ? 1 : 0;
-        issue_tile_copy(smem, a_tile, 0, wave, oa);
-        issue_tile_copy(smem + 16 * kPackBlock, w_tile, 0, wave, ow);
-        issue_tile_copy(smem + kStage, a_tile, (int64_t)b1 * a_kb, wave, oa);
-        issue_tile_copy(smem + kStage + 16 * kPackBlock, w_tile, (int64_t)b1 * w_kb, wave, ow);
-    }
-    for (int kb = 0; kb < nkb; ++kb) {
-        uint8_t* cur = smem + (kb & 1) * kStage;
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));  // this wave's copies of block kb have landed
-        barrier_no_fence();                           // ... and every other wave's
-        const uint8_t* la = cur + wm * 8 * kPackBlock + lane_off;
-        const uint8_t* lw = cur + (16 + wn * 8) * kPackBlock + lane_off;
-        // raw[g][t][half]: slice q = 2 (lane / 32) + g of tile t (W tiles 0..3, A tiles 4..7)
-        uint4 raw[2][8][2];
+    // Copies: waves 0, 1 fill A subtiles 0-7 / 8-15 of every slot, waves 2, 3 the W
+    // subtiles; 8 one-kilobyte copies per wave per half block.  o[j]: the lane's
+    // source offset of subtile 8 (wave % 2) + j at k block 0, half 0.
+    const bool cp_w = wave >= 2;
+    const bool cp_packed = cp_w ? kWPacked : kAPacked;
+    const int sub0 = 8 * (wave & 1);
+    uint32_t o[8];
+    {
+        const int64_t base_row = cp_w ? n_base : m_base;
+        const int rows = cp_w ? N : M;
+        const int r16 = lane & 15, kq = (lane >> 4) * 32;
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const uint8_t* p = (t < 4 ? lw + 2 * t * kPackBlock : la + 2 * (t - 4) * kPackBlock) + g * 256;
-                raw[g][t][0] = *reinterpret_cast<const uint4*>(p);
-                raw[g][t][1] = *reinterpret_cast<const uint4*>(p + 1024);
+        for (int j = 0; j < 8; ++j) {
+            const int js = sub0 + j;
+            if (cp_packed) {
+                int64_t t = (base_row >> 4) + js;
+                const int64_t last_tile = ((int64_t)rows + 15) / 16 - 1;
+                t = t < last_tile ? t : last_tile;
+                o[j] = (uint32_t)((t - (base_row >> 4)) * (int64_t)nkb * kPackBlock + 16 * lane);
+            } else {
+                int64_t r = base_row + 16 * js + r16;
+                r = r < rows ? r : rows - 1;
+                o[j] = (uint32_t)((r - base_row) * K + kq);
             }
-        auto step = [&](int g, int s4) __attribute__((always_inline)) {
-            bf16x8 v[8];
+        }
+    }
+    const uint8_t* src = cp_w ? (kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K)
+                              : (kAPacked ? A + (m_base >> 4) * (int64_t)nkb * kPackBlock : A + m_base * K);
+    const int64_t src_kb = cp_packed ? kPackBlock : 128;   // bytes per k block
+    const int64_t src_h = cp_packed ? 1024 : 16;           // bytes to the second half
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    const uint32_t dst_op = lds0 + (cp_w ? 16 * 1024u : 0u) + (uint32_t)sub0 * 1024u;
+
+    // copy j (0..7) of half block hb (clamped to the last one) into its slot
+    auto copy = [&](int j, int hb) __attribute__((always_inline)) {
+        hb = hb < nhb ? hb : nhb - 1;
+        const int64_t off = (int64_t)(hb >> 1) * src_kb + (int64_t)(hb & 1) * src_h;
+        copy16_to_lds(src + off + o[j], dst_op + (uint32_t)((hb & (kExSlots - 1)) * kExSlot + j * 1024));
+    };
+
+    // Fragment reads: tile t of the wave's W (t = 0..3) or A (t = 4..7) rows, slot
+    // part u (0, 1); the lane's 16 bytes of the half block.
+    const int lane_off = ((lane & 31) >> 4) * 1024 + (lane & 15) * 16 + (lane >> 5) * 512;
+    const uint8_t* rd_w = smem + 16 * 1024 + wn * 8 * 1024 + lane_off;
+    const uint8_t* rd_a = smem + wm * 8 * 1024 + lane_off;
+    uint4 raw[2][8][2];
+    auto read = [&](int b, int t, int u, int hb) __attribute__((always_inline)) {
+        const int slot = (hb & (kExSlots - 1)) * kExSlot;
+        const uint8_t* p = (t < 4 ? rd_w + 2048 * t : rd_a + 2048 * (t - 4)) + slot + 256 * u;
+        raw[b][t][u] = *reinterpret_cast<const uint4*>(p);
+    };
+    bf16x8 v[2][8];
+    auto widen = [&](int vb, int b, int t) __attribute__((always_inline)) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const uint4 r = raw[g][t][s4 >> 1];
-                v[t] = (s4 & 1) ? widen8(r.z, r.w) : widen8(r.x, r.y);
+        for (int f = 0; f < 8; ++f) {
+            const uint4 r = raw[b][f][t >> 1];
+            v[vb][f] = (t & 1) ? widen8(r.z, r.w) : widen8(r.x, r.y);
+        }
+    };
+
+    if (nhb > 0) {
+#pragma unroll
+        for (int h = 0; h < kExSlots; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) copy(j, h);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(24));   // this wave's copies of half block 0 have landed
+        barrier_no_fence();                           // ... and every other wave's
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) read(0, t, u, 0);
+        widen(0, 0, 0);
+    }
+
+    // Half block hb, its fragments in raw[b]: four steps of 16 k.  Step t issues
+    // two of the eight copies of hb + 4, steps 0 and 1 the reads of hb + 1 into
+    // raw[b ^ 1]; each step widens the next step's operands between its
+    // multiplies (step 3: step 0 of hb + 1).
+    auto half_block = [&](int hb, int b) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(16));
+        barrier_no_fence();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            copy(2 * t, hb + 4);
+            copy(2 * t + 1, hb + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t < 2) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) read(b ^ 1, 4 * t + q, u, hb + 1);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[i], v[4 + j], acc[i][j], 0, 0, 0);
-        };
-        step(0, 0);
-        __builtin_amdgcn_sched_barrier(0);   // the first step overlaps the remaining reads
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all of this wave's reads are done
-        barrier_no_fence();                  // ... and every other wave's: the stage may be refilled
-        const int n = kb + 2 < nkb ? kb + 2 : nkb - 1;
-        const int64_t a_off = (int64_t)n * a_kb, w_off = (int64_t)n * w_kb;
-        // Steps 1..7, with the 16 copies of block kb + 2 spread between them
-        // (3, 3, 2, 2, 2, 2, 2 before steps 1..7).
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[t & 1][i], v[t & 1][4 + j], acc[i][j], 0,
+                                                                        0, 0);
+            if (t < 3) widen((t + 1) & 1, b, t + 1);
+            else widen(0, b ^ 1, 0);
+            // issue order: each multiply followed by two converts (the reads first, one per multiply)
 #pragma unroll
-        for (int st = 1; st < 8; ++st) {
-            const int c0 = kCopySplit[st - 1], c1 = kCopySplit[st];
-#pragma unroll
-            for (int c = c0; c < c1; ++c) issue_stage_copy(c, cur, a_tile, w_tile, a_off, w_off, wave, oa, ow);
-            __builtin_amdgcn_sched_barrier(0);
-            step(st >> 2, st & 3);
+            for (int k = 0; k < 16; ++k) {
+                if (t < 2 && k < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    for (int hb = 0; hb < nhb; hb += 2) {
+        half_block(hb, 0);
+        half_block(hb + 1, 1);
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
 
     if (kOut == kOutBF16 || kOut == kOutE4M3) {
-        __syncthreads();  // every wave is done with the stages: the LDS now holds the output tiles
+        __syncthreads();  // every wave is done with the slots: the LDS now holds the output tiles
         uint8_t* wl = smem + wave * kEpiWaveBytes;
         const QScale q = out_qscale<kOut>(qs);
         float sam[4];
@@ -511,7 +587,7 @@ static hipError_t launch_big_t(const uint8_t* aq, const float* sa, int sa_pt, co
             <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per, qs);
     else
         gemm_big_exact<kOut, kWPacked, kAPacked>
-            <<<grid, block, 2 * 32 * kPackBlock, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per, qs);
+            <<<grid, block, kExSlots * kExSlot, stream>>>(aq, sa, sa_pt, wq, sw, y, M, N, K, per, qs);
     return hipGetLastError();
 }
 
