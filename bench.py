@@ -210,6 +210,32 @@ class ClockReader:
         except Exception as e:  # the reading is optional
             self.error = str(e)[:120]
 
+    def power_w(self):
+        """Socket power (W) now, or None."""
+        if self.handle is None:
+            return None
+        try:
+            p = self.api.amdsmi_get_power_info(self.handle)
+            for k in ("socket_power", "current_socket_power", "average_socket_power"):
+                v = p.get(k)
+                if isinstance(v, (int, float)) and 0 < v < 100000:
+                    return int(v)
+        except Exception:
+            pass
+        return None
+
+    def power_cap_w(self):
+        """The board's power cap (W), or None."""
+        if self.handle is None:
+            return None
+        try:
+            v = self.api.amdsmi_get_power_cap_info(self.handle).get("power_cap")
+            if isinstance(v, (int, float)) and v > 0:
+                return int(v / 1e6) if v > 1e5 else int(v)   # reported in microwatts
+        except Exception:
+            pass
+        return None
+
     def value(self):
         if self.handle is None:
             return None
@@ -231,10 +257,11 @@ class ClockReader:
             return None
 
 
-def sustained_clock(torch, clock, launch, launch_ms, seconds=2.5, settle=0.6, samples=6, gap=0.2):
+def sustained_clock(torch, clock, launch, launch_ms, seconds=2.5, settle=0.8, samples=6, gap=0.2, power=None):
     """Graphics clock while the GPU runs back-to-back launches of one kernel:
     about `seconds` of launches are queued, then after `settle` s the clock is
-    read `samples` times.  Returns (readings or None, ms per launch of the loop)."""
+    read `samples` times (and the socket power into the list `power`, if given).
+    Returns (readings or None, ms per launch of the loop)."""
     torch.cuda.synchronize()
     n = max(1, int(seconds * 1e3 / launch_ms))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -249,6 +276,10 @@ def sustained_clock(torch, clock, launch, launch_ms, seconds=2.5, settle=0.6, sa
             v = clock.value()
             if v:
                 vals.append(v)
+            if power is not None:
+                w = clock.power_w()
+                if w:
+                    power.append(w)
             time.sleep(gap)
     torch.cuda.synchronize()
     return (vals or None), a.elapsed_time(b) / n
@@ -345,7 +376,8 @@ def main():
     flops = 2.0 * M * N * K
     achieved = flops / (ks["mean_us"] * 1e-6) / 1e12
     clock = ClockReader(torch)
-    mhz, _ = sustained_clock(torch, clock, gemm_kernel, ks["mean_us"] * 1e-3)
+    watts = []
+    mhz, _ = sustained_clock(torch, clock, gemm_kernel, ks["mean_us"] * 1e-3, power=watts)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                 "kernel": "gemm_big_exact<bf16 out, packed W, row-major A> (exact accumulation on the bf16 matrix "
@@ -361,6 +393,9 @@ def main():
             achieved / (BF16_PEAK_TFLOPS * clk / PEAK_CLOCK_MHZ), 4)
     else:
         roofline["sustained_gfx_clock_mhz"] = None
+    # the matrix cores run this loop under the board's power cap, which sets the clock
+    roofline["socket_power_w_samples"] = watts or None
+    roofline["power_cap_w"] = clock.power_cap_w()
 
     details = [{"workload": "headline step: per-step durations", **stats(per_step)}]
     # the two arms' calls on their own, and the quantization kernels inside them
@@ -437,9 +472,10 @@ def large_rows(sg, torch, dev, T, x, xb_host, w_host, wq_rm, wp, sw, aq, sa, s_s
                           "exact", w_layout="packed", a_layout="row_major"))
     f = lambda i: sg.fp8_scaled_gemm(aq, sa, wp, sw, y=y, accum="mfma_fp8", w_layout="packed")
     ms = float(stats(T.per_call(f, warmup=3, min_calls=5, min_ms=1))["mean_us"]) * 1e-3
-    mhz, ms = sustained_clock(torch, clock, f, ms)
+    watts = []
+    mhz, ms = sustained_clock(torch, clock, f, ms, power=watts)
     row = {"workload": f"sustained graphics clock, large-layer GEMM {M}x{N}x{K} loop (FP8 matrix cores)",
-           "accum": "mfma_fp8", "mean_us": round(ms * 1e3, 1), "mhz_samples": mhz}
+           "accum": "mfma_fp8", "mean_us": round(ms * 1e3, 1), "mhz_samples": mhz, "socket_power_w_samples": watts}
     if mhz:
         clk = float(np.median(mhz))
         row["mhz_median"] = clk

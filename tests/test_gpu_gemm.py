@@ -122,14 +122,20 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
     assert np.array_equal(sw_got.view(np.uint32), sw_ref.view(np.uint32)), f"{what}: weight scales"
     assert_codes_equal(wq_got, wq_ref, f"{what}: weight codes")
 
+    # every output buffer starts as NaN: a tile the kernels skip (or a row or
+    # column they drop) leaves NaN behind, which the full-size check below finds
+    def nan_out(dtype):
+        return torch.full((M, N), float("nan"), dtype=dtype, device="cuda")
+
     y32_fused = None
     if static is None:
         sa_t = torch.empty(M, dtype=torch.float32, device="cuda")
-        y_t = sg.fp8_scaled_gemm(xt, sa_t, wg, sw_t, a_scale_mode="per_token", accum=accum, w_layout=layout)
+        y_t = sg.fp8_scaled_gemm(xt, sa_t, wg, sw_t, a_scale_mode="per_token", accum=accum, w_layout=layout,
+                                 y=nan_out(torch.bfloat16))
         if is_bf16 and sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", M, N, K) == 0:
             # quantized inside the decode kernel: the same kernel's fp32 output checks its epilogue
             y32_fused = sg.fp8_scaled_gemm(xt, None, wg, sw_t, out_dtype=torch.float32, accum=accum,
-                                           w_layout=layout)
+                                           w_layout=layout, y=nan_out(torch.float32))
         aq_ref, sa_ref = w8a8.quant_per_token(xf[rows])
         assert np.array_equal(host(sa_t)[rows].view(np.uint32), sa_ref.view(np.uint32)), f"{what}: act scales"
         # the accumulator through the same kernel: pre-quantized codes, unit scales, fp32 out
@@ -138,20 +144,27 @@ def gemm_case(x, w, *, rows=None, cols=None, accum="exact", static=None, what=""
     else:
         s = np.float32(static)
         sa_t = dev(np.float32([s]))
-        y_t = sg.fp8_scaled_gemm(xt, sa_t, wg, sw_t, a_scale_mode="per_tensor", accum=accum, w_layout=layout)
+        y_t = sg.fp8_scaled_gemm(xt, sa_t, wg, sw_t, a_scale_mode="per_tensor", accum=accum, w_layout=layout,
+                                 y=nan_out(torch.bfloat16))
         aq_ref = w8a8.quant_static(xf[rows], s)
         sa_ref = np.full(len(rows), s, np.float32)
         aq_t = sg.fp8_quant_per_tensor_static(xt, sa_t)
         assert_codes_equal(host(aq_t)[rows], aq_ref, f"{what}: act codes")
     ones_m = torch.ones(M, dtype=torch.float32, device="cuda")
     ones_n = torch.ones(N, dtype=torch.float32, device="cuda")
-    acc_t = sg.fp8_scaled_gemm(aq_t, ones_m, wg, ones_n, out_dtype=torch.float32, accum=accum, w_layout=layout)
+    acc_t = sg.fp8_scaled_gemm(aq_t, ones_m, wg, ones_n, out_dtype=torch.float32, accum=accum, w_layout=layout,
+                               y=nan_out(torch.float32))
     # the same codes in the fragment order (FP8SG_A_PACKED): the kernels give each
     # lane the same k, so the accumulators must agree bit for bit
     ap_t = sg.fp8_pack_weights(aq_t)
     acc_p = sg.fp8_scaled_gemm(ap_t, ones_m, wg, ones_n, out_dtype=torch.float32, accum=accum, w_layout=layout,
-                               a_layout="packed", a_shape=(M, K))
+                               a_layout="packed", a_shape=(M, K), y=nan_out(torch.float32))
     torch.cuda.synchronize()
+    # every output of every call was written (finite inputs give finite outputs)
+    for name, t in (("bf16 output", y_t), ("fp32 accumulator", acc_t), ("packed-A accumulator", acc_p),
+                    ("fused fp32 output", y32_fused)):
+        if t is not None:
+            assert not bool(torch.isnan(t.float()).any()), f"{what}: {name} has unwritten (NaN) outputs"
     y_bits = host_bits16(y_t)[np.ix_(rows, cols)]
     acc_gpu = host(acc_t)[np.ix_(rows, cols)]
     acc_pk = host(acc_p)[np.ix_(rows, cols)]
@@ -202,11 +215,24 @@ def test_ragged_tiles(m, n, k, accum, layout):
     gemm_case(bf16_bits_from_f32(x), w, accum=accum, what=f"ragged {m}x{n}x{k} {accum} {layout}", layout=layout)
 
 
-def _sample(M, N, seed, nr=40, nc=384):
+def _sample(M, N, seed, nr=40, nc=384, tile=256):
+    """Rows and columns to compare at full size: the first and last, one at random
+    inside every 256-row and every 256-column tile (so every output tile of the
+    large-tile kernels, and every tile of its per-XCD order, is compared at
+    least once), and nr / nc more at random."""
     rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, nr, replace=False)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, nc, replace=False)]))
+    per_r = [rng.integers(t, min(t + tile, M)) for t in range(0, M, tile)]
+    per_c = [rng.integers(t, min(t + tile, N)) for t in range(0, N, tile)]
+    rows = np.unique(np.concatenate([[0, M - 1], per_r, rng.choice(M, nr, replace=False)]).astype(np.int64))
+    cols = np.unique(np.concatenate([[0, N - 1], per_c, rng.choice(N, nc, replace=False)]).astype(np.int64))
     return rows, cols
+
+
+def test_sample_covers_every_output_tile():
+    for M, N in ((8192, 4096), (4096, 28672), (300, 1000)):
+        rows, cols = _sample(M, N, 3)
+        assert set(np.unique(rows // 256)) == set(range((M + 255) // 256))
+        assert set(np.unique(cols // 256)) == set(range((N + 255) // 256))
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -324,3 +350,59 @@ def test_fused_decode_quant(accum, layout):
     x = rng.standard_normal((4, 512)).astype(np.float32)
     w = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
     gemm_case(x, w, accum=accum, what=f"fp32 activations {accum} {layout}", layout=layout)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("m", [1, 4, 32, 300])
+def test_exact_mode_widens_every_code(m, layout):
+    """One-hot weights (code 0x38 = 1.0 at k = n) against activation rows that
+    hold every one of the 254 finite E4M3 codes: in exact mode each output is
+    exactly the decoded activation code, so the FP8 -> bf16 widening of every
+    code, both signs, subnormals and the maximum included, is checked bit for
+    bit (skinny kernels for M <= 32, the large-tile kernel above)."""
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert finite.size == 254
+    K = 256
+    rng = np.random.default_rng(m)
+    a = np.zeros((m, K), np.uint8)
+    for i in range(m):
+        a[i, :254] = rng.permutation(finite)
+    n = K
+    w = np.zeros((n, K), np.uint8)
+    w[np.arange(n), np.arange(n)] = 0x38
+    wt = dev(w)
+    wg = sg.fp8_pack_weights(wt) if layout == "packed" else wt
+    one_m = torch.ones(m, dtype=torch.float32, device="cuda")
+    one_n = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    sg.fp8_scaled_gemm(dev(a), one_m, wg, one_n, y=y, out_dtype=torch.float32, accum="exact", w_layout=layout)
+    torch.cuda.synchronize()
+    got = host(y).astype(np.float64)
+    want = fp8.decode(a)
+    assert np.array_equal(got, want), f"{int((got != want).sum())} outputs differ"
+    # the sign of zero is not asked for: the accumulator starts at +0
+
+
+@pytest.mark.parametrize("accum", ACCUMS)
+@pytest.mark.parametrize("m", [1, 4])
+def test_empty_reduction(m, accum):
+    """K = 0: an empty sum.  bf16 per-token activations with M <= 4 take the
+    two-kernel path (the row quantizer writes the unit scales), never the
+    decode kernel that quantizes inside the GEMM; every output is 0."""
+    n = 40
+    x = torch.empty((m, 0), dtype=torch.bfloat16, device="cuda")
+    wq = torch.empty((n, 0), dtype=torch.uint8, device="cuda")
+    sw = torch.full((n,), 3.0, dtype=torch.float32, device="cuda")
+    assert sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", m, n, 0) > 0
+    for out_dtype in (torch.bfloat16, torch.float32):
+        sa = torch.full((m,), float("nan"), dtype=torch.float32, device="cuda")
+        y = torch.full((m, n), float("nan"), dtype=out_dtype, device="cuda")
+        sg.fp8_scaled_gemm(x, sa, wq, sw, y=y, out_dtype=out_dtype, accum=accum)
+        torch.cuda.synchronize()
+        assert (host(sa) == 1.0).all()
+        assert (host(y.float()) == 0.0).all()
+    so = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+    q = torch.full((m, n), 0x7F, dtype=torch.uint8, device="cuda")
+    sg.fp8_scaled_gemm_fp8out(x, None, wq, sw, so, y=q, accum=accum)
+    torch.cuda.synchronize()
+    assert (host(q) == 0).all()

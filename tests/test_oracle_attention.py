@@ -108,3 +108,31 @@ def test_abs_weight_bounds_the_output():
     o = at.attention_decode(q, kq, vq, sk, sv, L)
     w = at.attention_abs_weight(q, kq, vq, sk, sv, L)
     assert (np.abs(o) <= w * (1 + 1e-12)).all()
+
+
+def test_abs_weight_is_the_output_of_the_absolute_values():
+    """sum_t p_t |V[t, d]| two-sided: with non-negative value codes it equals the
+    attention output itself (pinned against PyTorch's SDPA above), flipping value
+    signs leaves it unchanged, and it matches p @ |V| with p from PyTorch's own
+    float64 softmax of the scaled scores."""
+    q, kq, vq, sk, sv = _case(8)
+    L = np.array([96, 77])
+    v_pos = vq & np.uint8(0x7F)
+    w_pos = at.attention_abs_weight(q, kq, v_pos, sk, sv, L)
+    assert np.array_equal(w_pos, at.attention_decode(q, kq, v_pos, sk, sv, L))
+    w = at.attention_abs_weight(q, kq, vq, sk, sv, L)
+    assert np.array_equal(w, w_pos)
+    B, Hq, D = q.shape
+    G = Hq // kq.shape[2]
+    for b in range(B):
+        n = int(L[b])
+        K = torch.from_numpy(kq[b, :n]).view(torch.float8_e4m3fn).to(torch.float64) * \
+            torch.from_numpy(sk.astype(np.float64))[None, :, None]
+        V = torch.from_numpy(vq[b, :n]).view(torch.float8_e4m3fn).to(torch.float64).abs() * \
+            torch.from_numpy(sv.astype(np.float64))[None, :, None]
+        Kh = K.permute(1, 0, 2).repeat_interleave(G, dim=0)          # [Hq, n, D]
+        Vh = V.permute(1, 0, 2).repeat_interleave(G, dim=0)
+        Q = torch.from_numpy(q[b].astype(np.float64))[:, :, None]    # [Hq, D, 1]
+        p = torch.softmax((Kh @ Q)[:, :, 0] / np.sqrt(D), dim=-1)    # [Hq, n]
+        ref = (p[:, None, :] @ Vh)[:, 0, :].numpy()
+        np.testing.assert_allclose(w[b], ref, rtol=1e-12, atol=0)

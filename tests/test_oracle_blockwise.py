@@ -155,3 +155,30 @@ def test_abs_sum_bounds_the_value():
     # flipping the sign of one activation row flips that output row exactly
     y2 = bw.gemm_blockwise_exact(qa ^ np.uint8(0x80) * (np.arange(4) == 2)[:, None].astype(np.uint8), sa, qw, sw)
     assert np.array_equal(y2[2], -y[2]) and np.array_equal(np.delete(y2, 2, 0), np.delete(y, 2, 0))
+
+
+def test_abs_sum_in_exact_rationals_and_its_equality_case():
+    """sum_g |s_a[m, g] s_w[n / 128, g]| sum_{k in g} |a_k w_k| (the scale of the
+    block-wise accumulator tolerance) against exact rationals on a tiny case with a
+    ragged last weight block, and its equality with the block-wise value itself
+    when every code and scale is non-negative."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((2, 256)) * np.float32([[1.0], [30.0]])).astype(np.float32)
+    w = (rng.standard_normal((130, 256)) * 0.05).astype(np.float32)
+    w[129, 7] = 3.0
+    qa, sa = bw.quant_act_blockwise(x)
+    qw, sw = bw.quant_weight_blockwise(w)
+    s = bw.gemm_blockwise_abs(qa, sa, qw, sw)
+    a = fp8.decode(qa)
+    wv = fp8.decode(qw)
+    for m in range(2):
+        for n in (0, 1, 127, 128, 129):
+            tot = Fraction(0)
+            for g in range(2):
+                p = sum(abs(Fraction(float(a[m, k])) * Fraction(float(wv[n, k]))) for k in range(128 * g, 128 * g + 128))
+                tot += abs(Fraction(float(sa[m, g])) * Fraction(float(sw[n // 128, g]))) * p
+            assert abs(Fraction(float(s[m, n])) - tot) <= tot * Fraction(1, 2 ** 50)
+    a_pos, w_pos = qa & np.uint8(0x7F), qw & np.uint8(0x7F)
+    assert np.array_equal(bw.gemm_blockwise_abs(a_pos, sa, w_pos, sw), bw.gemm_blockwise_exact(a_pos, sa, w_pos, sw))
+    # the signs of the codes do not change it
+    assert np.array_equal(bw.gemm_blockwise_abs(a_pos, sa, w_pos, sw), s)

@@ -154,6 +154,30 @@ def test_gemm_exact_tiny_workload_against_fractions():
         assert got == nearest_bf16(yv)
 
 
+def test_gemm_abs_sum_against_fractions():
+    """sum_k |a_ik w_jk| -- the scale of the accumulator tolerance -- against exact
+    rationals on the tiny workload's codes, and two closed forms: where every
+    product is non-negative it equals the exact accumulator itself, and for
+    all-maximum codes it is K * 448^2."""
+    x, w = tiny_w8a8(0)
+    aq, _ = w8a8.quant_per_token(x)
+    wq, _ = w8a8.quant_weight_per_channel(w)
+    s = w8a8.gemm_abs_sum(aq, wq)
+    dec = {c: Fraction(float(E4M3.values[c])) for c in range(256) if np.isfinite(E4M3.values[c])}
+    rng = np.random.default_rng(12)
+    for _ in range(60):
+        i, j = int(rng.integers(16)), int(rng.integers(512))
+        exact = sum(abs(dec[int(aq[i, k])] * dec[int(wq[j, k])]) for k in range(256))
+        assert Fraction(float(s[i, j])) == exact
+    # clearing the sign bits makes every product non-negative: then sum|a w| is the sum itself
+    a_pos, w_pos = aq & np.uint8(0x7F), wq & np.uint8(0x7F)
+    assert np.array_equal(w8a8.gemm_abs_sum(aq, wq), w8a8.gemm_acc_exact(a_pos, w_pos))
+    assert np.array_equal(w8a8.gemm_abs_sum(a_pos, w_pos), w8a8.gemm_acc_exact(a_pos, w_pos))
+    k = 4096
+    big = w8a8.gemm_abs_sum(np.full((2, k), 0xFE, np.uint8), np.full((3, k), 0x7E, np.uint8))
+    assert (big == k * 448.0 * 448.0).all()
+
+
 def test_gemm_one_hot_weights_reproduce_activations():
     rng = np.random.default_rng(6)
     finite = np.array([c for c in range(256) if np.isfinite(E4M3.values[c])], dtype=np.uint8)
