@@ -109,7 +109,12 @@ typedef enum fp8sg_layout {
     FP8SG_A_PACKED = 2,
     /* fp8_quant_mx only: the E8M0 scales in the packed layout that
      * fp8_scaled_gemm_mx reads (see fp8_pack_mx_scales). */
-    FP8SG_MX_SCALES_PACKED = 4
+    FP8SG_MX_SCALES_PACKED = 4,
+    /* fp8_quant_per_token_group / fp8_scaled_gemm_blockwise only: the
+     * activation scales k-block-major, [K / 128, M] (s[g, m] at g * M + m),
+     * instead of [M, K / 128].  The large-tile block-wise GEMM then reads the
+     * scales of 64 consecutive rows of one k block as one contiguous run. */
+    FP8SG_SCALES_KMAJOR = 8
 } fp8sg_layout;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -289,8 +294,10 @@ fp8sg_status fp8_rmsnorm_quant_per_token(const void* x, int x_dtype, const void*
  *           (fp8_packed_weight_bytes(M, K) bytes; the padding rows of the last
  *           16-row tile are left unwritten)
  *   scales  [M, K / 128] fp32 (output), row-major:
- *           s[m, g] = RN32(max_{k in group g} |x[m, k]| / 448), or 1.0 when 0
- *   layout  0 or FP8SG_A_PACKED; other bits: FP8SG_E_DTYPE
+ *           s[m, g] = RN32(max_{k in group g} |x[m, k]| / 448), or 1.0 when 0;
+ *           with FP8SG_SCALES_KMAJOR the same values as [K / 128, M]
+ *   layout  0 or an OR of FP8SG_A_PACKED and FP8SG_SCALES_KMAJOR; other bits:
+ *           FP8SG_E_DTYPE
  *   K % 128 == 0.
  */
 fp8sg_status fp8_quant_per_token_group(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* q,
@@ -320,10 +327,11 @@ fp8sg_status fp8_quant_weight_blockwise(const void* w, int w_dtype, int64_t N, i
  *   P_g[m, n] = sum_{k = 128 g}^{128 g + 127} a_q[m, k] * w_q[n, k].
  *   a_q       [M, K] E4M3 codes (row-major, or FP8SG_A_PACKED fragment order)
  *   a_scales  [M, K / 128] fp32, as written by fp8_quant_per_token_group
+ *             ([K / 128, M] with FP8SG_SCALES_KMAJOR in layout)
  *   wq        [N, K] E4M3 codes (row-major, or FP8SG_W_PACKED fragment order)
  *   w_scales  [ceil(N / 128), K / 128] fp32, as written by fp8_quant_weight_blockwise
  *   y         [M, N] FP8SG_BF16 (y rounded to nearest even) or FP8SG_F32 (y)
- *   layout    0 or an OR of FP8SG_W_PACKED and FP8SG_A_PACKED
+ *   layout    0 or an OR of FP8SG_W_PACKED, FP8SG_A_PACKED and FP8SG_SCALES_KMAJOR
  *   accum     FP8SG_ACCUM_MFMA_FP8: each P_g is one FP8 matrix-core product
  *             (with that hardware's in-instruction alignment, see fp8sg_accum);
  *             FP8SG_ACCUM_EXACT: P_g formed exactly on the bf16 matrix cores,

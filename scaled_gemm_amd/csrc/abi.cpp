@@ -299,14 +299,15 @@ fp8sg_status fp8_scaled_gemm_fp8out(const void* a, int a_dtype, float* a_scales,
 fp8sg_status fp8_quant_per_token_group(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* q, float* scales,
                                        int layout, void* stream) {
     if (!is_hp(x_dtype)) return FP8SG_E_DTYPE;
-    if (layout != 0 && layout != FP8SG_A_PACKED) return FP8SG_E_DTYPE;
+    if ((layout & ~(FP8SG_A_PACKED | FP8SG_SCALES_KMAJOR)) != 0) return FP8SG_E_DTYPE;
     if (M < 0 || K < 0 || M >= kMaxDim || K >= kMaxDim || K % 128 != 0) return FP8SG_E_SHAPE;
     if (M == 0 || K == 0) return FP8SG_OK;
     if (!x || !q || !scales) return FP8SG_E_NULL;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8SG_E_ALIGN;
     fp8sg_status d = device_ok();
     if (d != FP8SG_OK) return d;
-    return launched(fp8sg::launch_group_quant(x, x_dtype == FP8SG_BF16, M, K, q, scales, layout == FP8SG_A_PACKED,
+    return launched(fp8sg::launch_group_quant(x, x_dtype == FP8SG_BF16, M, K, q, scales,
+                                              (layout & FP8SG_A_PACKED) != 0, (layout & FP8SG_SCALES_KMAJOR) != 0,
                                               (hipStream_t)stream));
 }
 
@@ -329,7 +330,7 @@ fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales
                                        int accum, void* stream) {
     if (!(y_dtype == FP8SG_BF16 || y_dtype == FP8SG_F32)) return FP8SG_E_DTYPE;
     if (!(accum == FP8SG_ACCUM_EXACT || accum == FP8SG_ACCUM_MFMA_FP8)) return FP8SG_E_DTYPE;
-    if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED)) != 0) return FP8SG_E_DTYPE;
+    if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED | FP8SG_SCALES_KMAJOR)) != 0) return FP8SG_E_DTYPE;
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxGemmK) return FP8SG_E_SHAPE;
     if (K % 128 != 0) return FP8SG_E_SHAPE;
     if (accum == FP8SG_ACCUM_EXACT && M > 32) return FP8SG_E_DTYPE;  // exact partials: skinny kernel only
@@ -341,7 +342,8 @@ fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales
     fp8sg_status d = device_ok();
     if (d != FP8SG_OK) return d;
     // K == 0 launches too: the kernels read no scale and write the empty sums (zeros)
-    return launched(fp8sg::launch_gemm_blockwise(a_q, (layout & FP8SG_A_PACKED) != 0, a_scales, wq,
+    return launched(fp8sg::launch_gemm_blockwise(a_q, (layout & FP8SG_A_PACKED) != 0, a_scales,
+                                                 (layout & FP8SG_SCALES_KMAJOR) != 0, wq,
                                                  (layout & FP8SG_W_PACKED) != 0, w_scales, y, y_dtype == FP8SG_BF16,
                                                  M, N, K, accum == FP8SG_ACCUM_MFMA_FP8, (hipStream_t)stream));
 }

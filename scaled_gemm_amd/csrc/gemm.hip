@@ -44,17 +44,18 @@ hipError_t launch_gemm(const uint8_t* aq, bool a_packed, const float* a_scales, 
                            fp8_mfma, stream);
 }
 
-hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* a_scales, const uint8_t* wq,
-                                 bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N,
-                                 int64_t K, bool fp8_mfma, hipStream_t stream) {
+hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* a_scales, bool sa_kmajor,
+                                 const uint8_t* wq, bool w_packed, const float* w_scales, void* y, bool y_bf16,
+                                 int64_t M, int64_t N, int64_t K, bool fp8_mfma, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const int m = (int)M, n = (int)N, k = (int)K;
     if (M <= 32)
-        return launch_skinny_blockwise(aq, a_packed, a_scales, wq, w_packed, w_scales, y, y_bf16, m, n, k, fp8_mfma,
-                                       stream);
+        return launch_skinny_blockwise(aq, a_packed, a_scales, sa_kmajor, wq, w_packed, w_scales, y, y_bf16, m, n, k,
+                                       fp8_mfma, stream);
     // exact block-wise accumulation exists for M <= 32 only (checked by the ABI)
     if (!fp8_mfma) return hipErrorInvalidValue;
-    return launch_big_blockwise(aq, a_packed, a_scales, wq, w_packed, w_scales, y, y_bf16, m, n, k, stream);
+    return launch_big_blockwise(aq, a_packed, a_scales, sa_kmajor, wq, w_packed, w_scales, y, y_bf16, m, n, k,
+                                stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -432,7 +432,7 @@ constexpr int kBwCopies = 9;                  // copies per wave per stage
 
 template <int kOut, bool kWPacked, bool kAPacked>
 __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __restrict__ A,
-                                                             const float* __restrict__ sa,
+                                                             const float* __restrict__ sa, int sa_kmajor,
                                                              const uint8_t* __restrict__ W,
                                                              const float* __restrict__ sw, void* __restrict__ Y,
                                                              int M, int N, int K, int tiles_per_xcd,
@@ -463,11 +463,15 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
                               : (kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K);
     const int64_t src_kb = cp_a ? (kAPacked ? kPackBlock : 128) : (kWPacked ? kPackBlock : 128);
     const uint32_t dst_op = cp_a ? 0u : (uint32_t)(16 * kPackBlock);
+    // s_a [M, K/128] row-major, or k-block-major [K/128, M] (sa_kmajor): then the 64
+    // scales a wave copies per k block are 256 contiguous bytes instead of 64 lines
     const float* ssrc;
+    int64_t sstep = 1;
     if (cp_a) {
         int64_t m = m_base + 64 * wave + lane;
         m = m < M ? m : M - 1;
-        ssrc = sa + m * nkb;
+        ssrc = sa_kmajor ? sa + m : sa + m * nkb;
+        sstep = sa_kmajor ? (int64_t)M : 1;
     } else {
         int64_t nb = (n_base >> 7) + (lane & 1);
         nb = nb < nbw ? nb : nbw - 1;
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
             const int q = (wave & 3) * 8 + c, j = q >> 1, h = q & 1;
             copy16_to_lds(src + (int64_t)kb * src_kb + o[c], stage + dst_op + (uint32_t)(j * kPackBlock + h * 1024));
         } else {
-            copy4_to_lds(ssrc + kb, stage + dst_sc);
+            copy4_to_lds(ssrc + kb * sstep, stage + dst_sc);
         }
     };
 
@@ -623,18 +627,21 @@ hipError_t launch_big_gemm(const uint8_t* aq, bool a_packed, const float* sa, in
 }
 
 template <int kOut, bool kWPacked, bool kAPacked>
-static hipError_t launch_big_bw_t(const uint8_t* aq, const float* sa, const uint8_t* wq, const float* sw, void* y,
-                                  int M, int N, int K, hipStream_t stream) {
+static hipError_t launch_big_bw_t(const uint8_t* aq, const float* sa, int sa_kmajor, const uint8_t* wq,
+                                  const float* sw, void* y, int M, int N, int K, hipStream_t stream) {
     const int tiles = ((M + kBig - 1) / kBig) * ((N + kBig - 1) / kBig);
     const int per = (tiles + 7) / 8;
-    gemm_big_blockwise<kOut, kWPacked, kAPacked>
-        <<<dim3((unsigned)(per * 8)), dim3(512), 2 * kBwStage, stream>>>(aq, sa, wq, sw, y, M, N, K, per, nullptr);
+    gemm_big_blockwise<kOut, kWPacked, kAPacked><<<dim3((unsigned)(per * 8)), dim3(512), 2 * kBwStage, stream>>>(
+        aq, sa, sa_kmajor, wq, sw, y, M, N, K, per, nullptr);
     return hipGetLastError();
 }
 
-hipError_t launch_big_blockwise(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq, bool w_packed,
-                                const float* sw, void* y, bool y_bf16, int M, int N, int K, hipStream_t stream) {
-#define FP8SG_BW(YB, WP, AP) launch_big_bw_t<(YB) ? kOutBF16 : kOutF32, WP, AP>(aq, sa, wq, sw, y, M, N, K, stream)
+hipError_t launch_big_blockwise(const uint8_t* aq, bool a_packed, const float* sa, bool sa_kmajor, const uint8_t* wq,
+                                bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
+                                hipStream_t stream) {
+    const int km = sa_kmajor ? 1 : 0;
+#define FP8SG_BW(YB, WP, AP) \
+    launch_big_bw_t<(YB) ? kOutBF16 : kOutF32, WP, AP>(aq, sa, km, wq, sw, y, M, N, K, stream)
     if (y_bf16) {
         if (a_packed) return w_packed ? FP8SG_BW(true, true, true) : FP8SG_BW(true, false, true);
         return w_packed ? FP8SG_BW(true, true, false) : FP8SG_BW(true, false, false);

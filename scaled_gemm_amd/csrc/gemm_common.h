@@ -14,14 +14,15 @@ namespace fp8sg {
 hipError_t launch_skinny_gemm(const uint8_t* aq, bool a_packed, const float* sa, int sa_per_token, const uint8_t* wq,
                               bool w_packed, const float* sw, void* y, int out_kind, const float* out_scale, int M,
                               int N, int K, bool fp8_mfma, hipStream_t stream);
-hipError_t launch_skinny_blockwise(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq,
-                                   bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
-                                   bool fp8_mfma, hipStream_t stream);
+hipError_t launch_skinny_blockwise(const uint8_t* aq, bool a_packed, const float* sa, bool sa_kmajor,
+                                   const uint8_t* wq, bool w_packed, const float* sw, void* y, bool y_bf16, int M,
+                                   int N, int K, bool fp8_mfma, hipStream_t stream);
 hipError_t launch_big_gemm(const uint8_t* aq, bool a_packed, const float* sa, int sa_per_token, const uint8_t* wq,
                            bool w_packed, const float* sw, void* y, int out_kind, const float* out_scale, int M, int N,
                            int K, bool fp8_mfma, hipStream_t stream);
-hipError_t launch_big_blockwise(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq, bool w_packed,
-                                const float* sw, void* y, bool y_bf16, int M, int N, int K, hipStream_t stream);
+hipError_t launch_big_blockwise(const uint8_t* aq, bool a_packed, const float* sa, bool sa_kmajor, const uint8_t* wq,
+                                bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
+                                hipStream_t stream);
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -34,7 +34,8 @@ namespace fp8sg {
 // are added in a fixed order through LDS, so the result does not depend on
 // timing.
 //
-// kBlock: block-wise scales, sa [M, K / 128] and sw [ceil(N / 128), K / 128].
+// kBlock: block-wise scales, sa [M, K / 128] (or, when the int argument
+// sa_per_token is 1, k-block-major [K / 128, M]) and sw [ceil(N / 128), K / 128].
 // Each k block's 16 x 16 partial products start from zero, are multiplied by
 // s_a[m, kb] * s_w[n / 128, kb] and added to the fp32 accumulator, so the
 // epilogue only rounds.  A 16-row subtile never straddles a 128-row block.
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
 #pragma unroll
         for (int t = 0; t < kMT; ++t) {
             const int m = 16 * t + r16 < M ? 16 * t + r16 : M - 1;
-            sa_row[t] = sa + (int64_t)m * nkb;
+            sa_row[t] = sa_per_token ? sa + m : sa + (int64_t)m * nkb;
         }
 #pragma unroll
         for (int s = 0; s < kNS; ++s) {
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(64 * kKS) void gemm_skinny(const uint8_t* __restric
                                         : load_frag_global(arow[t] + off);
                 if (kBlock) {
 #pragma unroll
-                    for (int t = 0; t < kMT; ++t) fa[d][t] = sa_row[t][kb];
+                    for (int t = 0; t < kMT; ++t) fa[d][t] = sa_row[t][sa_per_token ? (int64_t)kb * M : kb];
 #pragma unroll
                     for (int s = 0; s < kNS; ++s) fw[d][s] = sw_row[s][kb];
                 }
@@ -273,25 +274,25 @@ hipError_t launch_skinny_gemm(const uint8_t* aq, bool a_packed, const float* sa,
 }
 
 template <bool kFp8, int kOut, bool kWPacked, bool kAPacked>
-static hipError_t launch_skinny_bw_t(const uint8_t* aq, const float* sa, const uint8_t* wq, const float* sw, void* y,
-                                     int M, int N, int K, hipStream_t stream) {
+static hipError_t launch_skinny_bw_t(const uint8_t* aq, const float* sa, int sa_kmajor, const uint8_t* wq,
+                                     const float* sw, void* y, int M, int N, int K, hipStream_t stream) {
     dim3 block(64 * SKINNY_KS);
     dim3 grid((unsigned)((N + 16 * SKINNY_NS - 1) / (16 * SKINNY_NS)));
     if (M <= 16)
         gemm_skinny<kFp8, kOut, 1, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
-            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K, nullptr);
+            <<<grid, block, 0, stream>>>(aq, sa, sa_kmajor, wq, sw, y, M, N, K, nullptr);
     else
         gemm_skinny<kFp8, kOut, 2, SKINNY_NS, SKINNY_KS, SKINNY_DEPTH, kWPacked, kAPacked, true>
-            <<<grid, block, 0, stream>>>(aq, sa, 1, wq, sw, y, M, N, K, nullptr);
+            <<<grid, block, 0, stream>>>(aq, sa, sa_kmajor, wq, sw, y, M, N, K, nullptr);
     return hipGetLastError();
 }
 
 template <bool kFp8>
-static hipError_t launch_skinny_bw_m(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq,
-                                     bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
-                                     hipStream_t stream) {
+static hipError_t launch_skinny_bw_m(const uint8_t* aq, bool a_packed, const float* sa, bool sa_kmajor,
+                                     const uint8_t* wq, bool w_packed, const float* sw, void* y, bool y_bf16, int M,
+                                     int N, int K, hipStream_t stream) {
 #define FP8SG_BW(YB, WP, AP) \
-    launch_skinny_bw_t<kFp8, (YB) ? kOutBF16 : kOutF32, WP, AP>(aq, sa, wq, sw, y, M, N, K, stream)
+    launch_skinny_bw_t<kFp8, (YB) ? kOutBF16 : kOutF32, WP, AP>(aq, sa, sa_kmajor ? 1 : 0, wq, sw, y, M, N, K, stream)
     if (y_bf16) {
         if (a_packed) return w_packed ? FP8SG_BW(true, true, true) : FP8SG_BW(true, false, true);
         return w_packed ? FP8SG_BW(true, true, false) : FP8SG_BW(true, false, false);
@@ -301,11 +302,12 @@ static hipError_t launch_skinny_bw_m(const uint8_t* aq, bool a_packed, const flo
 #undef FP8SG_BW
 }
 
-hipError_t launch_skinny_blockwise(const uint8_t* aq, bool a_packed, const float* sa, const uint8_t* wq,
-                                   bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
-                                   bool fp8_mfma, hipStream_t stream) {
-    if (fp8_mfma) return launch_skinny_bw_m<true>(aq, a_packed, sa, wq, w_packed, sw, y, y_bf16, M, N, K, stream);
-    return launch_skinny_bw_m<false>(aq, a_packed, sa, wq, w_packed, sw, y, y_bf16, M, N, K, stream);
+hipError_t launch_skinny_blockwise(const uint8_t* aq, bool a_packed, const float* sa, bool sa_kmajor,
+                                   const uint8_t* wq, bool w_packed, const float* sw, void* y, bool y_bf16, int M,
+                                   int N, int K, bool fp8_mfma, hipStream_t stream) {
+    if (fp8_mfma)
+        return launch_skinny_bw_m<true>(aq, a_packed, sa, sa_kmajor, wq, w_packed, sw, y, y_bf16, M, N, K, stream);
+    return launch_skinny_bw_m<false>(aq, a_packed, sa, sa_kmajor, wq, w_packed, sw, y, y_bf16, M, N, K, stream);
 }
 
 // ---------------------------------------------------------------------------

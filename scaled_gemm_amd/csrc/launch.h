@@ -21,10 +21,11 @@ hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K,
 hipError_t launch_rmsnorm_quant(const void* x, bool x_is_bf16, const void* gamma, float eps, int64_t M, int64_t K,
                                 uint8_t* q, float* scales, float* y_out, bool packed, hipStream_t stream);
 
-// Block-wise dynamic quantization: activations in 1 x 128 groups (scales [M, K/128]),
-// weights in 128 x 128 blocks (scales [ceil(N/128), K/128]); K % 128 == 0.
+// Block-wise dynamic quantization: activations in 1 x 128 groups (scales [M, K/128],
+// or [K/128, M] with scales_kmajor), weights in 128 x 128 blocks (scales
+// [ceil(N/128), K/128]); K % 128 == 0.
 hipError_t launch_group_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
-                              bool packed, hipStream_t stream);
+                              bool packed, bool scales_kmajor, hipStream_t stream);
 hipError_t launch_block_quant_weight(const void* w, bool w_is_bf16, int64_t N, int64_t K, uint8_t* q, float* scales,
                                      hipStream_t stream);
 
@@ -46,10 +47,11 @@ hipError_t launch_gemm_fused_quant(const uint16_t* x, float* sa_out, const uint8
                                    const float* w_scales, void* y, int out_kind, const float* out_scale, int64_t M,
                                    int64_t N, int64_t K, bool fp8_mfma, hipStream_t stream);
 
-// Block-wise scaled GEMM: a_scales [M, K/128], w_scales [ceil(N/128), K/128].
-hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* a_scales, const uint8_t* wq,
-                                 bool w_packed, const float* w_scales, void* y, bool y_bf16, int64_t M, int64_t N,
-                                 int64_t K, bool fp8_mfma, hipStream_t stream);
+// Block-wise scaled GEMM: a_scales [M, K/128] (or [K/128, M] with sa_kmajor),
+// w_scales [ceil(N/128), K/128].
+hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* a_scales, bool sa_kmajor,
+                                 const uint8_t* wq, bool w_packed, const float* w_scales, void* y, bool y_bf16,
+                                 int64_t M, int64_t N, int64_t K, bool fp8_mfma, hipStream_t stream);
 
 // MXFP8: E8M0 scale bytes per 32 consecutive k (fmt 0 = E4M3, 1 = E5M2).  Scales
 // row-major [R, K / 32] or in the GEMM's packed layout; codes row-major or in

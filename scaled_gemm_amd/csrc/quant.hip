@@ -248,7 +248,8 @@ hipError_t launch_rmsnorm_quant(const void* x, bool x_is_bf16, const void* gamma
 // scales[m * (K / 128) + g] = RN32(amax / 448) (1.0 for an all-zero group).
 template <typename InT, bool kPacked>
 __global__ __launch_bounds__(256) void group_quant(const InT* __restrict__ x, int64_t K, int64_t nchunks,
-                                                   uint8_t* __restrict__ q, float* __restrict__ scales) {
+                                                   uint8_t* __restrict__ q, float* __restrict__ scales, int64_t M,
+                                                   int kmajor) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
         float v[8];
@@ -259,7 +260,11 @@ __global__ __launch_bounds__(256) void group_quant(const InT* __restrict__ x, in
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
         const float s = dynamic_scale(amax, kE4M3Max);
-        if ((c & 15) == 0) scales[c >> 4] = s;
+        if ((c & 15) == 0) {
+            // group g = c / 16 is (row g / nkb, k block g % nkb): row-major [M, K/128] or k-block-major [K/128, M]
+            const int64_t g = c >> 4, nkb = K >> 7;
+            scales[kmajor ? (g % nkb) * M + g / nkb : g] = s;
+        }
         const QScale p = make_qscale(s, kE4M3Max);
         uint8_t* dst;
         if (kPacked) {
@@ -273,18 +278,19 @@ __global__ __launch_bounds__(256) void group_quant(const InT* __restrict__ x, in
 }
 
 hipError_t launch_group_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
-                              bool packed, hipStream_t stream) {
+                              bool packed, bool scales_kmajor, hipStream_t stream) {
     const int64_t nchunks = M * (K / 8);
     if (nchunks == 0) return hipSuccess;
     int64_t blocks = (nchunks + 255) / 256;
     if (blocks > 256 * 16) blocks = 256 * 16;
     dim3 grid((unsigned)blocks), block(256);
+    const int km = scales_kmajor ? 1 : 0;
     if (x_is_bf16) {
-        if (packed) group_quant<uint16_t, true><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nchunks, q, scales);
-        else group_quant<uint16_t, false><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nchunks, q, scales);
+        if (packed) group_quant<uint16_t, true><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nchunks, q, scales, M, km);
+        else group_quant<uint16_t, false><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nchunks, q, scales, M, km);
     } else {
-        if (packed) group_quant<float, true><<<grid, block, 0, stream>>>((const float*)x, K, nchunks, q, scales);
-        else group_quant<float, false><<<grid, block, 0, stream>>>((const float*)x, K, nchunks, q, scales);
+        if (packed) group_quant<float, true><<<grid, block, 0, stream>>>((const float*)x, K, nchunks, q, scales, M, km);
+        else group_quant<float, false><<<grid, block, 0, stream>>>((const float*)x, K, nchunks, q, scales, M, km);
     }
     return hipGetLastError();
 }

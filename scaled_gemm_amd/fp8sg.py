@@ -27,7 +27,7 @@ OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_DEVICE, E_LAUNCH, E_WORKSPACE, E_SCRATC
 SCRATCH_BYTES = 16 << 20  # FP8SG_SCRATCH_BYTES
 F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
 SCALE_PER_TOKEN, SCALE_PER_TENSOR = 0, 1
-W_ROW_MAJOR, W_PACKED, A_PACKED, MX_SCALES_PACKED = 0, 1, 2, 4
+W_ROW_MAJOR, W_PACKED, A_PACKED, MX_SCALES_PACKED, SCALES_KMAJOR = 0, 1, 2, 4, 8
 ACCUM_EXACT, ACCUM_MFMA_FP8 = 0, 1
 
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
@@ -291,20 +291,24 @@ def fp8_scaled_gemm_fp8out(a: torch.Tensor, a_scales: Optional[torch.Tensor], wq
 
 
 def fp8_quant_per_token_group(x: torch.Tensor, layout="row_major", q: Optional[torch.Tensor] = None,
-                              scales: Optional[torch.Tensor] = None, stream=None):
+                              scales: Optional[torch.Tensor] = None, scale_layout="row_major", stream=None):
     """x [M, K] (bf16/fp32) -> (codes, scales [M, K / 128] fp32): one scale per
     token and 128-element group.  layout="packed": the codes in the fragment
-    order (1-D, fp8_packed_weight_bytes(M, K) bytes)."""
+    order (1-D, fp8_packed_weight_bytes(M, K) bytes).  scale_layout="kmajor":
+    the scales as [K / 128, M]."""
     _need(x, "x", _HP)
     M, K = x.shape
     packed = _LAYOUT[layout] == W_PACKED
+    kmajor = scale_layout == "kmajor"
     qshape = (fp8_packed_weight_bytes(M, K),) if packed else (M, K)
+    sshape = (K // 128, M) if kmajor else (M, K // 128)
     q = torch.empty(qshape, dtype=torch.uint8, device=x.device) if q is None else q
-    scales = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if scales is None else scales
+    scales = torch.empty(sshape, dtype=torch.float32, device=x.device) if scales is None else scales
     _need(q, "q", (torch.uint8,), qshape)
-    _need(scales, "scales", (torch.float32,), (M, K // 128))
+    _need(scales, "scales", (torch.float32,), sshape)
     _check(lib().fp8_quant_per_token_group(_ptr(x), _hp_code(x), M, K, _ptr(q), _ptr(scales),
-                                           A_PACKED if packed else 0, _stream(stream)), "fp8_quant_per_token_group")
+                                           (A_PACKED if packed else 0) | (SCALES_KMAJOR if kmajor else 0),
+                                           _stream(stream)), "fp8_quant_per_token_group")
     return q, scales
 
 
@@ -326,12 +330,14 @@ def fp8_quant_weight_blockwise(w: torch.Tensor, wq: Optional[torch.Tensor] = Non
 def fp8_scaled_gemm_blockwise(a: torch.Tensor, a_scales: torch.Tensor, wq: torch.Tensor, w_scales: torch.Tensor, *,
                               out_dtype=torch.bfloat16, accum="mfma_fp8", w_layout="row_major", a_layout="row_major",
                               a_shape: Optional[tuple] = None, w_shape: Optional[tuple] = None,
-                              y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                              y: Optional[torch.Tensor] = None, a_scale_layout="row_major",
+                              stream=None) -> torch.Tensor:
     """Y [M, N] = sum_g diag(s_a[:, g]) (A_q W_q^T)_g diag(s_w[n // 128, g]).
 
     a: E4M3 codes [M, K] (or the packed 1-D buffer with a_shape=(M, K));
     a_scales [M, K/128]; wq [N, K] (or packed with w_shape=(N, K));
-    w_scales [ceil(N/128), K/128].  accum="exact" needs M <= 32."""
+    w_scales [ceil(N/128), K/128].  accum="exact" needs M <= 32.
+    a_scale_layout="kmajor": a_scales is [K/128, M]."""
     _need(a, "a", (torch.uint8,))
     _need(wq, "wq", (torch.uint8,))
     a_packed = _LAYOUT[a_layout] == W_PACKED
@@ -344,12 +350,13 @@ def fp8_scaled_gemm_blockwise(a: torch.Tensor, a_scales: torch.Tensor, wq: torch
         raise ValueError("w_layout='packed' takes w_shape=(N, K) and fp8_packed_weight_bytes(N, K) bytes")
     if not w_packed and wq.shape[1] != K:
         raise ValueError(f"wq has shape {tuple(wq.shape)}, expected K = {K}")
-    _need(a_scales, "a_scales", (torch.float32,), (M, K // 128))
+    kmajor = a_scale_layout == "kmajor"
+    _need(a_scales, "a_scales", (torch.float32,), (K // 128, M) if kmajor else (M, K // 128))
     _need(w_scales, "w_scales", (torch.float32,), ((N + 127) // 128, K // 128))
     y_code = {torch.bfloat16: BF16, torch.float32: F32}[out_dtype]
     y = torch.empty((M, N), dtype=out_dtype, device=a.device) if y is None else y
     _need(y, "y", (out_dtype,), (M, N))
-    layout = (W_PACKED if w_packed else 0) | (A_PACKED if a_packed else 0)
+    layout = (W_PACKED if w_packed else 0) | (A_PACKED if a_packed else 0) | (SCALES_KMAJOR if kmajor else 0)
     _check(lib().fp8_scaled_gemm_blockwise(_ptr(a), _ptr(a_scales), _ptr(wq), layout, _ptr(w_scales), _ptr(y), y_code,
                                            M, N, K, _ACCUM[accum], _stream(stream)), "fp8_scaled_gemm_blockwise")
     return y

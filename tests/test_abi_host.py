@@ -54,6 +54,9 @@ def test_blockwise_validation(lib):
     assert lib.fp8_quant_per_token_group(A, b.BF16, 4, 64, A, A, 0, None) == b.E_SHAPE
     assert lib.fp8_quant_per_token_group(A, b.E4M3, 4, 128, A, A, 0, None) == b.E_DTYPE
     assert lib.fp8_quant_per_token_group(A, b.BF16, 4, 128, A, A, b.W_PACKED, None) == b.E_DTYPE
+    assert lib.fp8_quant_per_token_group(A, b.BF16, 4, 128, A, A, b.MX_SCALES_PACKED, None) == b.E_DTYPE
+    # the k-block-major scale layout is accepted (it fails later only for lack of a device)
+    assert lib.fp8_quant_per_token_group(None, b.BF16, 0, 128, None, None, b.SCALES_KMAJOR | b.A_PACKED, None) == b.OK
     assert lib.fp8_quant_per_token_group(A, b.BF16, 4, 128, A, None, 0, None) == b.E_NULL
     assert lib.fp8_quant_per_token_group(A + 4, b.BF16, 4, 128, A, A, 0, None) == b.E_ALIGN
     assert lib.fp8_quant_per_token_group(None, b.BF16, 0, 128, None, None, 0, None) == b.OK
@@ -67,6 +70,8 @@ def test_blockwise_validation(lib):
     assert g(A, A, A, 0, A, A, b.BF16, 33, 8, 128, b.ACCUM_EXACT, None) == b.E_DTYPE
     assert g(A, A, A, 0, A, A, b.BF16, 4, 8, 100, b.ACCUM_MFMA_FP8, None) == b.E_SHAPE
     assert g(A, A, A, 4, A, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_DTYPE
+    assert g(A, A, A, 16, A, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_DTYPE
+    assert g(None, None, None, b.SCALES_KMAJOR, None, None, b.BF16, 0, 8, 128, b.ACCUM_MFMA_FP8, None) == b.OK
     assert g(A, A, A, 0, A, A, b.E4M3, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_DTYPE
     assert g(A, None, A, 0, A, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_NULL
     assert g(A, A, A, 0, A + 2, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_ALIGN

@@ -99,9 +99,11 @@ def check_gemm(y_f32, y_bits, aq, sa, wq, sw, cols, accum, what):
     assert (d[cancel] <= ulp[cancel] + 1e-5 * T[cancel]).all()
 
 
-def run_case(x, w, *, accum, rows=None, cols=None, w_layout="row_major", a_layout="row_major", what=""):
+def run_case(x, w, *, accum, rows=None, cols=None, w_layout="row_major", a_layout="row_major", what="",
+             kmajor=False):
     """Quantize X (1 x 128 groups) and W (128 x 128 blocks) on the GPU, check
-    codes and scales against the oracle, run the GEMM, check its outputs."""
+    codes and scales against the oracle, run the GEMM, check its outputs.
+    kmajor: the activation scales travel k-block-major ([K/128, M])."""
     is_bf16 = x.dtype == np.uint16
     xt = dev_bf16(x) if is_bf16 else dev(x)
     xf = f32_from_bf16_bits(x) if is_bf16 else x
@@ -110,11 +112,13 @@ def run_case(x, w, *, accum, rows=None, cols=None, w_layout="row_major", a_layou
     rows = np.arange(M) if rows is None else np.asarray(rows)
     cols = np.arange(N) if cols is None else np.asarray(cols)
 
-    aq_t, sa_t = sg.fp8_quant_per_token_group(xt)
+    sl = "kmajor" if kmajor else "row_major"
+    aq_t, sa_t = sg.fp8_quant_per_token_group(xt, scale_layout=sl)
     wq_t, sw_t = sg.fp8_quant_weight_blockwise(dev(w))
     aq_ref, sa_ref = bw.quant_act_blockwise(xf[rows])
     sw_ref = bw.weight_block_scales(w)
-    aq_got, sa_got, sw_got = host(aq_t)[rows], host(sa_t)[rows], host(sw_t)
+    sa_host = host(sa_t).T if kmajor else host(sa_t)
+    aq_got, sa_got, sw_got = host(aq_t)[rows], sa_host[rows], host(sw_t)
     assert np.array_equal(sa_got.view(np.uint32), sa_ref.view(np.uint32)), f"{what}: activation group scales"
     assert_codes_equal(aq_got, aq_ref, f"{what}: activation codes")
     assert np.array_equal(sw_got.view(np.uint32), sw_ref.view(np.uint32)), f"{what}: weight block scales"
@@ -125,18 +129,26 @@ def run_case(x, w, *, accum, rows=None, cols=None, w_layout="row_major", a_layou
 
     a_in = aq_t if a_layout == "row_major" else sg.fp8_pack_weights(aq_t)
     w_in = wq_t if w_layout == "row_major" else sg.fp8_pack_weights(wq_t)
-    kw = dict(accum=accum, w_layout=w_layout, a_layout=a_layout, a_shape=(M, K), w_shape=(N, K))
-    y32 = sg.fp8_scaled_gemm_blockwise(a_in, sa_t, w_in, sw_t, out_dtype=torch.float32, **kw)
-    y16 = sg.fp8_scaled_gemm_blockwise(a_in, sa_t, w_in, sw_t, **kw)
+    kw = dict(accum=accum, w_layout=w_layout, a_layout=a_layout, a_shape=(M, K), w_shape=(N, K), a_scale_layout=sl)
+    # outputs start as NaN: an output the kernels do not write stays NaN and fails below
+    y32 = sg.fp8_scaled_gemm_blockwise(a_in, sa_t, w_in, sw_t, out_dtype=torch.float32,
+                                       y=torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda"), **kw)
+    y16 = sg.fp8_scaled_gemm_blockwise(a_in, sa_t, w_in, sw_t,
+                                       y=torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda"), **kw)
     torch.cuda.synchronize()
+    assert not bool(torch.isnan(y32).any()) and not bool(torch.isnan(y16.float()).any()), f"{what}: unwritten outputs"
     check_gemm(host(y32)[np.ix_(rows, cols)], host_bits16(y16)[np.ix_(rows, cols)], aq_ref, sa_ref, wq_all, sw_ref,
                cols, accum, what)
 
 
-def _sample(M, N, seed, nr=24, nc=256):
+def _sample(M, N, seed, nr=24, nc=256, tile=256):
+    """First and last rows / columns, one at random inside every 256-row and
+    256-column tile (every output tile of the large-tile kernel), and more at random."""
     rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(nr, M), replace=False)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(nc, N), replace=False)]))
+    per_r = [rng.integers(t, min(t + tile, M)) for t in range(0, M, tile)]
+    per_c = [rng.integers(t, min(t + tile, N)) for t in range(0, N, tile)]
+    rows = np.unique(np.concatenate([[0, M - 1], per_r, rng.choice(M, min(nr, M), replace=False)]).astype(np.int64))
+    cols = np.unique(np.concatenate([[0, N - 1], per_c, rng.choice(N, min(nc, N), replace=False)]).astype(np.int64))
     return rows, cols
 
 
@@ -152,13 +164,15 @@ def test_tiny(accum, layout):
 def test_decode(m, accum):
     xb, w, _ = decode_inputs(m)
     _, cols = _sample(m, w.shape[0], m, nc=1024)
-    run_case(xb, w, accum=accum, cols=cols, w_layout="packed", a_layout="packed", what=f"decode M={m} {accum}")
+    run_case(xb, w, accum=accum, cols=cols, w_layout="packed", a_layout="packed", what=f"decode M={m} {accum}",
+             kmajor=(m == 8))
 
 
+@pytest.mark.parametrize("kmajor", [False, True], ids=["scales_row_major", "scales_kmajor"])
 @pytest.mark.parametrize("layout", ["row_major", "packed"])
 @pytest.mark.parametrize("m,n,k", [(300, 1000, 1024), (129, 1001, 256), (33, 4100, 512), (17, 515, 128),
                                    (1, 7, 128), (5, 1, 384), (256, 384, 2048), (520, 130, 384)])
-def test_ragged(m, n, k, layout):
+def test_ragged(m, n, k, layout, kmajor):
     rng = np.random.default_rng(m * 7 + n + k)
     x = rng.standard_normal((m, k)).astype(np.float32)
     x[:, rng.integers(0, k, 3)] *= 40
@@ -168,16 +182,17 @@ def test_ragged(m, n, k, layout):
     w[: min(n, 128), :128] *= 30                                     # one block with larger weights
     accums = ["mfma_fp8", "exact"] if m <= 32 else ["mfma_fp8"]
     for accum in accums:
-        run_case(bf16_bits_from_f32(x), w, accum=accum, w_layout=layout, a_layout=layout,
-                 what=f"ragged {m}x{n}x{k} {accum} {layout}")
+        run_case(bf16_bits_from_f32(x), w, accum=accum, w_layout=layout, a_layout=layout, kmajor=kmajor,
+                 what=f"ragged {m}x{n}x{k} {accum} {layout} kmajor={kmajor}")
 
 
+@pytest.mark.parametrize("kmajor", [False, True], ids=["scales_row_major", "scales_kmajor"])
 @pytest.mark.parametrize("k", [4096, 14336])
-def test_prefill_sampled(k):
+def test_prefill_sampled(k, kmajor):
     xb, w, _ = prefill_inputs(k)
     rows, cols = _sample(xb.shape[0], w.shape[0], k)
     run_case(xb, w, accum="mfma_fp8", rows=rows, cols=cols, w_layout="packed", a_layout="row_major",
-             what=f"prefill K={k}")
+             what=f"prefill K={k} kmajor={kmajor}", kmajor=kmajor)
 
 
 def test_fp32_input_and_packed_codes():
