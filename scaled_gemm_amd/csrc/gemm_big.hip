@@ -419,13 +419,16 @@ __global__ __launch_bounds__(256, 1) void gemm_big_exact(const uint8_t* __restri
 // LDS two at a time, which keeps the wave within 256 registers.
 //
 // Staging as in the per-token kernels (direct global-to-LDS copies in fragment
-// order, two stages, copies two k blocks ahead, fence-free barriers), with
-// the copies split by operand: waves 0-3 copy the A tile, waves 4-7 the W
-// tile, 8 one-kilobyte copies each.  Each wave also copies one 4-byte value
-// per lane of the block's scales: waves 0-3 the s_a of tile rows 64 w + lane,
-// waves 4-7 the s_w of the tile's two 128-column blocks (lane % 2), so every
-// wave has 9 copies per stage.  A stage is refilled once every wave has read
-// all of it (the W fragments are read until the last row of multiplies).
+// order, two stages, copies two k blocks ahead, fence-free barriers).  A stage
+// is released in two parts, so its refill is spread over the k block instead
+// of following its last read in one burst (a burst of copies holds up the
+// multiplies queued behind it): the A tile, the scales and the W subtiles of
+// rows 0-3 (each wave's W fragments 0-3) are read by row 3, and after a
+// barrier there their copies for block kb + 2 are issued over rows 3-6; the W
+// subtiles of rows 4-7 are read by row 7 and are copied after the barrier
+// there.  Every wave makes 4 one-kilobyte A copies, 2 + 2 W copies and one
+// 4-byte-per-lane copy of scales: waves 0-3 the s_a of tile rows 64 w + lane,
+// waves 4-7 the s_w of the tile's two 128-column blocks (lane % 2).
 constexpr int kBwOps = 32 * kPackBlock;       // A 32 KB + W 32 KB
 constexpr int kBwStage = kBwOps + 2048;       // + s_a (256 floats) + s_w (4 x 64 floats)
 constexpr int kBwCopies = 9;                  // copies per wave per stage
@@ -454,15 +457,48 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // this wave's copies: 8 kilobytes of one operand tile and 256 bytes of scales
+    // This wave's copies per stage: c = 0..3 the A (subtile, half) pairs 4 wave + c;
+    // c = 4, 5 W pairs of rows 0-3 (subtiles 0-3 and 8-11), c = 6, 7 W pairs of
+    // rows 4-7 (subtiles 4-7 and 12-15); c = 8 the scales.  o[c]: the lane's
+    // source offset at k block 0; d[c]: the destination offset in a stage.
     const bool cp_a = wave < 4;
-    uint32_t o[8];
-    if (cp_a) tile_copy_offsets<kAPacked>(o, m_base, M, K, wave & 3, lane);
-    else tile_copy_offsets<kWPacked>(o, n_base, N, K, wave & 3, lane);
-    const uint8_t* src = cp_a ? (kAPacked ? A + (m_base >> 4) * (int64_t)nkb * kPackBlock : A + m_base * K)
-                              : (kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K);
-    const int64_t src_kb = cp_a ? (kAPacked ? kPackBlock : 128) : (kWPacked ? kPackBlock : 128);
-    const uint32_t dst_op = cp_a ? 0u : (uint32_t)(16 * kPackBlock);
+    uint32_t o[8], d[8];
+    {
+        auto pair = [&](int c, int& sub, int& half) __attribute__((always_inline)) {
+            if (c < 4) {
+                sub = (4 * wave + c) >> 1;
+                half = c & 1;
+            } else {
+                const int q = 2 * wave + (c & 1);                    // 0..15 within the row half
+                const int j = q >> 1;                                 // 0..7
+                sub = (j & 3) + ((j >> 2) << 3) + (c >= 6 ? 4 : 0);   // {0-3, 8-11} or {4-7, 12-15}
+                half = q & 1;
+            }
+        };
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            int sub, half;
+            pair(c, sub, half);
+            const bool is_a = c < 4;
+            const bool packed = is_a ? kAPacked : kWPacked;
+            const int64_t base_row = is_a ? m_base : n_base;
+            const int rows = is_a ? M : N;
+            if (packed) {
+                int64_t t = (base_row >> 4) + sub;
+                const int64_t last_tile = ((int64_t)rows + 15) / 16 - 1;
+                t = t < last_tile ? t : last_tile;
+                o[c] = (uint32_t)((t - (base_row >> 4)) * (int64_t)nkb * kPackBlock + 1024 * half + 16 * lane);
+            } else {
+                int64_t r = base_row + 16 * sub + (lane & 15);
+                r = r < rows ? r : rows - 1;
+                o[c] = (uint32_t)((r - base_row) * K + (lane >> 4) * 32 + 16 * half);
+            }
+            d[c] = (uint32_t)((is_a ? 0 : 16 * kPackBlock) + sub * kPackBlock + half * 1024);
+        }
+    }
+    const uint8_t* a_src = kAPacked ? A + (m_base >> 4) * (int64_t)nkb * kPackBlock : A + m_base * K;
+    const uint8_t* w_src = kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K;
+    const int64_t a_kb = kAPacked ? kPackBlock : 128, w_kb = kWPacked ? kPackBlock : 128;
     // s_a [M, K/128] row-major, or k-block-major [K/128, M] (sa_kmajor): then the 64
     // scales a wave copies per k block are 256 contiguous bytes instead of 64 lines
     const float* ssrc;
@@ -482,13 +518,14 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
 
     // copy c (0..8) of block kb into the stage at LDS address `stage`
     auto issue_copy = [&](int c, uint32_t stage, int kb) __attribute__((always_inline)) {
-        if (c < 8) {
-            const int q = (wave & 3) * 8 + c, j = q >> 1, h = q & 1;
-            copy16_to_lds(src + (int64_t)kb * src_kb + o[c], stage + dst_op + (uint32_t)(j * kPackBlock + h * 1024));
-        } else {
-            copy4_to_lds(ssrc + kb * sstep, stage + dst_sc);
-        }
+        if (c < 4) copy16_to_lds(a_src + (int64_t)kb * a_kb + o[c], stage + d[c]);
+        else if (c < 8) copy16_to_lds(w_src + (int64_t)kb * w_kb + o[c], stage + d[c]);
+        else copy4_to_lds(ssrc + kb * sstep, stage + dst_sc);
     };
+    // copies issued before rows 3..7 of a k block: [kBwSplit[i - 3], kBwSplit[i - 2]) -- rows 3-6 the
+    // A, scale and first-half W copies (c = 0..5, 8), row 7 the second-half W copies (c = 6, 7)
+    constexpr int kBwOrder[kBwCopies] = {0, 1, 4, 2, 3, 5, 8, 6, 7};
+    constexpr int kBwSplit[6] = {0, 2, 4, 6, 7, 9};
 
     if (nkb > 0) {
         const int b1 = nkb > 1 ? 1 : 0;
@@ -516,14 +553,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
         const int nxt = kb + 2 < nkb ? kb + 2 : nkb - 1;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if (i < 7) {
-                wf[(i + 1) & 1] = load_frag_packed(lw + (i + 1) * kPackBlock, lane);
-            } else {
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the stage are done
-                barrier_no_fence();                  // ... and every other wave's: refill it with block kb + 2
-#pragma unroll
-                for (int c = 0; c < kBwCopies; ++c) issue_copy(c, cur_lds, nxt);
+            if (i == 3 || i == 7) {
+                // every wave's reads of the stage's A tile, scales and W rows 0-3 (row 3) or
+                // of the rest of it (row 7) are done: that part may be refilled with block kb + 2
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads
+                barrier_no_fence();                  // ... and every other wave's
             }
+            if (i >= 3) {
+#pragma unroll
+                for (int c = kBwSplit[i - 3]; c < kBwSplit[i - 2]; ++c) issue_copy(kBwOrder[c], cur_lds, nxt);
+            }
+            if (i < 7) wf[(i + 1) & 1] = load_frag_packed(lw + (i + 1) * kPackBlock, lane);
             __builtin_amdgcn_sched_barrier(0);
             // the products of W fragment i, then the scaled adds of fragment i - 1, whose
             // products were issued a row earlier: no add waits for its multiply
