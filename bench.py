@@ -66,10 +66,10 @@ PEAK_CLOCK_MHZ = 2400.0        # the clock of the published peaks
 TRAFFIC = {"kernel": "gemm_big_exact<1, true, false> at 4096x28672x8192",
            "sources": ("scaled_gemm_amd/csrc/gemm_big.hip", "scaled_gemm_amd/csrc/gemm_common.h",
                        "scaled_gemm_amd/csrc/fp8_device.h"),
-           "sha256": ("019f787b49ad81a08914f830587670e8f6459347457220f79e29956b632f42df",
-                      "89988b7a08724e97afd6856fd885427340a82060cced107b6d687ad8b1cc68d0",
-                      "0d2b00789594dec510b6f2e4e0550571f66e7a453f59b99894367fce3213d427"),
-           "fetch_kib": 688646.0, "write_kib": 229376.0,
+           "sha256": ("4859cce4f2a3013b0c4ab781804ac36adc21192b04c5de0ef50f3832061d3f74",
+                      "9d8772489a50975e9bef4239a0d80a5d5a9b6bc06d45b99dea934e9b3f721834",
+                      "3995d5f1aeacc4692dd13a666aa64d28c436a937ad879d464ad4a126345ca691"),
+           "fetch_kib": 688644.0, "write_kib": 229376.0,
            "fetch_factor": 1048576.0 / 524299.5, "write_factor": 1048576.0 / 1048576.0}
 LARGE_M, LARGE_N, LARGE_K = 4096, 28672, 8192
 DEC_N, DEC_K = 14336, 4096
