@@ -215,6 +215,26 @@ def test_ragged_tiles(m, n, k, accum, layout):
     gemm_case(bf16_bits_from_f32(x), w, accum=accum, what=f"ragged {m}x{n}x{k} {accum} {layout}", layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("accum", ACCUMS)
+@pytest.mark.parametrize("m,n,k", [(1, 7, 128), (5, 1000, 384), (16, 515, 4096), (17, 130, 1152), (32, 14336, 4096)])
+def test_decode_static_scale_in_call(m, n, k, accum, layout):
+    """A given per-tensor activation scale with M <= 32: the call quantizes X
+    straight into the fragment order (rows padded to 16) before the decode
+    GEMM, so the codes, the accumulator and the bf16 output all go through that
+    quantizer; scales cover a calibrated one, heavy saturation and underflow."""
+    from workloads import bf16_bits_from_f32
+    rng = np.random.default_rng(m * 31 + n + k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, rng.integers(0, k, 3)] *= 40
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    xb = bf16_bits_from_f32(x)
+    amax = float(np.max(np.abs(f32_from_bf16_bits(xb))))
+    for s in (np.float32(amax) / np.float32(448.0), np.float32(amax) / np.float32(4000.0), np.float32(amax)):
+        gemm_case(xb, w, accum=accum, static=np.float32(s), layout=layout,
+                  what=f"decode static {m}x{n}x{k} s={s!r} {accum} {layout}")
+
+
 def _sample(M, N, seed, nr=40, nc=384, tile=256):
     """Rows and columns to compare at full size: the first and last, one at random
     inside every 256-row and every 256-column tile (so every output tile of the
