@@ -147,7 +147,8 @@ def test_gemm_validation(lib):
     assert call(y=A + 4) == b.E_ALIGN
     assert call(M=0) == b.OK
     # a bf16 activation needs the workspace the size query reports: the codes
-    # (fragment order, rows padded to 16, for M <= 32; row-major above), then
+    # (fragment order, rows padded to 16, for M <= 32 and for every per-tensor
+    # scale; per-token rows above 32 row-major), then
     # the per-token scales -- except bf16 per-token with M <= 4 and K <= 4096,
     # which the decode kernel quantizes itself (no workspace)
     assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4, 8, 128) == 0
@@ -160,7 +161,8 @@ def test_gemm_validation(lib):
     assert lib.fp8_scaled_gemm_workspace_size(b.E4M3, b.SCALE_PER_TOKEN, 4, 8, 128) == 0
     assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TENSOR, 4, 8, 128) == 16 * 128
     assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TENSOR, 17, 8, 256) == 32 * 256
-    assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TENSOR, 33, 8, 256) == 33 * 256
+    assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TENSOR, 33, 8, 256) == 48 * 256
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TENSOR, 4096, 8, 8192) == 4096 * 8192
     assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 33, 8, 128) == 4352 + 256  # 33 * 128 rounded up to 256
     assert call(a_dt=b.BF16, sa=None, M=12) == b.E_WORKSPACE
     assert call(a_dt=b.BF16, sa=None, M=12, ws=A, wsb=need - 1) == b.E_WORKSPACE
