@@ -18,7 +18,7 @@ step's 2 x 2MNK flops divided by its time, in TFLOP/s; inputs are resident in
 HBM before the timed region starts.
 
 `roofline` is for the step's dominant kernel, the large-tile exact GEMM at that
-shape (gemm_big_exact, packed W, row-major A as the call's workspace holds it),
+shape (gemm_big_exact, packed W, packed A as the call's workspace holds it),
 timed per launch with HIP events on the library's stream over >= 100 back-to-back
 launches on pre-quantized A.  It is priced against the dense FP8 matrix-core
 peak (5.0 PFLOP/s); the bf16 matrix cores that exact accumulation runs on
@@ -63,13 +63,13 @@ PEAK_CLOCK_MHZ = 2400.0        # the clock of the published peaks
 # on this part, WRITE_SIZE all of them).  Valid only for the kernel source it
 # was measured on: when the hash of these files differs, traffic is reported
 # as null until the counters are taken again.
-TRAFFIC = {"kernel": "gemm_big_exact<1, true, false> at 4096x28672x8192",
+TRAFFIC = {"kernel": "gemm_big_exact<1, true, true> at 4096x28672x8192",
            "sources": ("scaled_gemm_amd/csrc/gemm_big.hip", "scaled_gemm_amd/csrc/gemm_common.h",
                        "scaled_gemm_amd/csrc/fp8_device.h"),
            "sha256": ("4859cce4f2a3013b0c4ab781804ac36adc21192b04c5de0ef50f3832061d3f74",
                       "9d8772489a50975e9bef4239a0d80a5d5a9b6bc06d45b99dea934e9b3f721834",
                       "3995d5f1aeacc4692dd13a666aa64d28c436a937ad879d464ad4a126345ca691"),
-           "fetch_kib": 688644.0, "write_kib": 229376.0,
+           "fetch_kib": 688646.5, "write_kib": 229376.0,
            "fetch_factor": 1048576.0 / 524299.5, "write_factor": 1048576.0 / 1048576.0}
 LARGE_M, LARGE_N, LARGE_K = 4096, 28672, 8192
 DEC_N, DEC_K = 14336, 4096
@@ -374,11 +374,14 @@ def main():
 
     # ------------------------------------------------------------ dominant kernel
     log("roofline kernel")
-    aq, sa = sg.fp8_quant_per_token(x)  # the codes the dynamic arm's call writes to its workspace
+    # the codes the dynamic arm's call writes to its workspace: the fragment order (packed A)
+    aq_rm, sa = sg.fp8_quant_per_token(x)
+    aq = sg.fp8_pack_weights(aq_rm)
+    del aq_rm
     torch.cuda.synchronize()
 
     def gemm_kernel(i):
-        sg.fp8_scaled_gemm(aq, sa, wp, sw, y=y_dyn, w_layout="packed")
+        sg.fp8_scaled_gemm(aq, sa, wp, sw, y=y_dyn, w_layout="packed", a_layout="packed", a_shape=(M, K))
 
     d = T.per_call(gemm_kernel, warmup=10, min_calls=100)
     ks = stats(d)
@@ -389,7 +392,7 @@ def main():
     mhz = None if clock is None else sustained_clock(torch, clock, gemm_kernel, ks["mean_us"] * 1e-3, power=watts)[0]
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
-                "kernel": "gemm_big_exact<bf16 out, packed W, row-major A> (exact accumulation on the bf16 matrix "
+                "kernel": "gemm_big_exact<bf16 out, packed W, packed A> (exact accumulation on the bf16 matrix "
                           "cores), 4096x28672x8192",
                 "flops_per_launch": flops, "avg_launch_us": ks["mean_us"], "launch_stats": ks,
                 "bf16_matrix_core_peak": BF16_PEAK_TFLOPS,

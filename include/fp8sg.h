@@ -105,7 +105,8 @@ typedef enum fp8sg_layout {
     /* A_q (a_dtype FP8SG_E4M3 only) in the same fragment order, e.g. from
      * fp8_pack_weights applied to [M, K] codes: ceil(M / 16) * 16 * K bytes.
      * Activations that fp8_scaled_gemm quantizes itself go to its workspace
-     * in this order when M <= 32 or the activation scale is per-tensor. */
+     * in this order when M <= 32, when the activation scale is per-tensor, and
+     * for per-token scales when K <= 8192 (bf16) or K <= 4096 (fp32). */
     FP8SG_A_PACKED = 2,
     /* fp8_quant_mx only: the E8M0 scales in the packed layout that
      * fp8_scaled_gemm_mx reads (see fp8_pack_mx_scales). */
@@ -178,8 +179,9 @@ fp8sg_status fp8_pack_weights(const uint8_t* wq, int64_t N, int64_t K, uint8_t* 
 /*
  * Bytes of device workspace fp8_scaled_gemm needs for these arguments: the
  * codes it quantizes, in the fragment order with rows padded to a multiple of
- * 16 when M <= 32 or the scale is per-tensor, row-major otherwise, then
- * (per-token mode without a caller buffer) the scales.  0 when the activation arrives already quantized, and
+ * 16 when M <= 32, when the scale is per-tensor, or when K <= 8192 (bf16) /
+ * K <= 4096 (fp32), row-major otherwise, then (per-token mode without a
+ * caller buffer) the scales.  0 when the activation arrives already quantized, and
  * for bf16 per-token activations with M <= 4 and K <= 4096, which the decode
  * kernel quantizes itself (in LDS, while its weight loads are in flight).
  * Host-only; no HIP call.

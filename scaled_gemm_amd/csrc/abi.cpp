@@ -122,20 +122,22 @@ fp8sg_status fp8_quant_per_tensor_static(const void* x, int x_dtype, int64_t num
 }
 
 // Activation codes quantized by fp8_scaled_gemm itself go to the workspace,
-// then the scales.  They are written in the fragment order (rows padded to 16)
-// for decode-sized activations (M <= 32: the skinny kernel reads all of A in
-// every workgroup) and for every per-tensor static scale (its quantizer writes
-// whole kilobytes of the fragment order at the speed of the row-major pass, and
-// the large-tile GEMM on packed A measured ~2% faster at 4096 x 28672 x 8192).
-// Larger per-token activations stay row-major: there one workgroup quantizes
-// one row, and in the fragment order its stores scatter over 16-byte pieces
-// (66 us instead of 20 us for [4096, 8192]).
+// then the scales, in the fragment order (rows padded to 16) wherever a
+// quantizer writes that order at full speed: decode-sized activations (M <= 32;
+// the skinny kernel reads all of A in every workgroup), every per-tensor static
+// scale (whole kilobytes of the order per wave), and per-token rows in 16-row
+// tiles when a tile's rows fit in registers (bf16 K <= 8192, fp32 K <= 4096:
+// 23 us against 20 us row-major for [4096, 8192], while the large-tile exact
+// GEMM on packed A measured 2-6% faster at 4096 x 28672 x 8192).  Other
+// per-token activations stay row-major.
 constexpr int64_t kPackedAMaxM = 32;
 
-bool quantized_a_packed(bool per_token, int64_t M) { return M <= kPackedAMaxM || !per_token; }
+bool quantized_a_packed(bool per_token, bool x_is_bf16, int64_t M, int64_t K) {
+    return M <= kPackedAMaxM || !per_token || fp8sg::row_quant_tiles_fit(x_is_bf16, K);
+}
 
-size_t quantized_a_bytes(bool per_token, int64_t M, int64_t K) {
-    const int64_t rows = quantized_a_packed(per_token, M) ? (M + 15) / 16 * 16 : M;
+size_t quantized_a_bytes(bool per_token, bool x_is_bf16, int64_t M, int64_t K) {
+    const int64_t rows = quantized_a_packed(per_token, x_is_bf16, M, K) ? (M + 15) / 16 * 16 : M;
     return align256((size_t)rows * (size_t)K);
 }
 
@@ -145,7 +147,7 @@ size_t fp8_scaled_gemm_workspace_size(int a_dtype, int a_scale_mode, int64_t M, 
     // decode-sized per-token activations are quantized inside the GEMM kernel itself
     if (a_scale_mode == FP8SG_SCALE_PER_TOKEN && fp8sg::gemm_fused_quant_fits(a_dtype == FP8SG_BF16, M, K)) return 0;
     const bool per_token = a_scale_mode == FP8SG_SCALE_PER_TOKEN;
-    size_t bytes = quantized_a_bytes(per_token, M, K);
+    size_t bytes = quantized_a_bytes(per_token, a_dtype == FP8SG_BF16, M, K);
     if (per_token) bytes += align256((size_t)M * 4);
     return bytes;
 }
@@ -223,7 +225,7 @@ fp8sg_status scaled_gemm_impl(const void* a, int a_dtype, float* a_scales, int a
     if (K > 0 && (!a || !wq)) return FP8SG_E_NULL;
     const bool per_token = a_scale_mode == FP8SG_SCALE_PER_TOKEN;
     const bool quantize_here = is_hp(a_dtype);
-    const bool pack_here = quantize_here && quantized_a_packed(per_token, M);
+    const bool pack_here = quantize_here && quantized_a_packed(per_token, a_dtype == FP8SG_BF16, M, K);
     if (!quantize_here || !per_token) {
         if (!a_scales) return FP8SG_E_NULL;  // an input in these modes
     }
@@ -257,8 +259,12 @@ fp8sg_status scaled_gemm_impl(const void* a, int a_dtype, float* a_scales, int a
         uint8_t* ws_q = (uint8_t*)workspace;
         hipError_t e;
         if (per_token) {
-            float* sc = a_scales ? a_scales : (float*)((uint8_t*)workspace + quantized_a_bytes(true, M, K));
-            e = fp8sg::launch_row_quant(a, a_dtype == FP8SG_BF16, M, K, ws_q, sc, pack_here, s);
+            float* sc = a_scales ? a_scales
+                                 : (float*)((uint8_t*)workspace + quantized_a_bytes(true, a_dtype == FP8SG_BF16, M, K));
+            if (pack_here && M > kPackedAMaxM)
+                e = fp8sg::launch_row_quant_tiles(a, a_dtype == FP8SG_BF16, M, K, ws_q, sc, s);
+            else
+                e = fp8sg::launch_row_quant(a, a_dtype == FP8SG_BF16, M, K, ws_q, sc, pack_here, s);
             sa = sc;
         } else if (pack_here) {
             e = fp8sg::launch_static_quant_packed(a, a_dtype == FP8SG_BF16, M, K, a_scales, ws_q, s);

@@ -16,6 +16,12 @@ constexpr int kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2;
 hipError_t launch_row_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
                             bool packed, hipStream_t stream);
 
+// Per-token quantization of [M, K] straight into the fragment order (rows padded
+// to 16), one workgroup per 16-row tile, for the K that row_quant_tiles_fit accepts.
+bool row_quant_tiles_fit(bool x_is_bf16, int64_t K);
+hipError_t launch_row_quant_tiles(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
+                                  hipStream_t stream);
+
 // RMSNorm fused with per-token E4M3 quantization of its output (K <= 16384);
 // gamma has x's dtype; y_out (optional) receives the fp32 normalised rows.
 hipError_t launch_rmsnorm_quant(const void* x, bool x_is_bf16, const void* gamma, float eps, int64_t M, int64_t K,

@@ -139,6 +139,128 @@ __global__ __launch_bounds__(256) void row_quant_stream(const InT* __restrict__ 
     }
 }
 
+// Per-row quantization straight into the fragment order for rows in whole
+// 16-row tiles: one workgroup of 16 waves per tile; wave w takes the k blocks
+// w, w + 16, ... (kKb of them) and lane l the 32 elements of row l % 16 at
+// 32 (l / 16) in each, which are exactly the bytes of that lane's two 16-byte
+// halves of the block (packed_offset).  The row maxima reduce over the four
+// lanes of a row (shuffles) and over the waves (LDS); the elements stay in
+// registers, and every store instruction writes one contiguous kilobyte.  Rows
+// past M are read as row M - 1 and not stored.
+template <typename InT, int kKb>
+__global__ __launch_bounds__(1024) void row_quant_tile16(const InT* __restrict__ x, int64_t M, int64_t K,
+                                                         uint8_t* __restrict__ q, float* __restrict__ scales) {
+    constexpr int kWords = (int)sizeof(InT) * 2;   // 16-byte words per 32 elements: 4 (bf16) or 8 (fp32)
+    constexpr int kPerWord = 32 / kWords;           // elements per word
+    __shared__ float red[16][16];                   // [wave][row]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nkb = K >> 7;
+    const int r16 = lane & 15;
+    int64_t row = ((int64_t)blockIdx.x << 4) + r16;
+    const bool live = row < M;
+    row = live ? row : M - 1;
+    const InT* xr = x + row * K + 32 * (lane >> 4);
+    uint4 d[kKb][kWords];
+#pragma unroll
+    for (int i = 0; i < kKb; ++i) {
+        int64_t kb = wave + 16 * i;
+        kb = kb < nkb ? kb : nkb - 1;   // a clamped (repeated) block is loaded but neither counted nor stored
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) d[i][w] = *reinterpret_cast<const uint4*>(xr + kb * 128 + w * kPerWord);
+    }
+    auto unpack8 = [&](const uint4& a, float (&v)[8]) __attribute__((always_inline)) {
+        if constexpr (sizeof(InT) == 2) {
+            v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+            v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+        }
+    };
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kKb; ++i) {
+        if (wave + 16 * i < nkb) {
+#pragma unroll
+            for (int w = 0; w < kWords; ++w) {
+                if constexpr (sizeof(InT) == 2) {
+                    float v[8];
+                    unpack8(d[i][w], v);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
+                } else {
+                    amax = fmaxf(amax, fmaxf(fmaxf(__builtin_fabsf(__uint_as_float(d[i][w].x)),
+                                                   __builtin_fabsf(__uint_as_float(d[i][w].y))),
+                                             fmaxf(__builtin_fabsf(__uint_as_float(d[i][w].z)),
+                                                   __builtin_fabsf(__uint_as_float(d[i][w].w)))));
+                }
+            }
+        }
+    }
+    // the four lanes of a row: l, l + 16, l + 32, l + 48
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (lane < 16) red[wave][lane] = amax;
+    __syncthreads();
+    amax = red[0][r16];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) amax = fmaxf(amax, red[w][r16]);
+    // keep the raw words, not their unpacked floats, live into the encode pass
+#pragma unroll
+    for (int i = 0; i < kKb; ++i)
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) opaque_words(d[i][w]);
+    const float s = dynamic_scale(amax, kE4M3Max);
+    if (wave == 0 && lane < 16 && live) scales[row] = s;
+    const QScale p = make_qscale(s, kE4M3Max);
+    if (!live) return;   // no barrier below
+#pragma unroll
+    for (int i = 0; i < kKb; ++i) {
+        const int64_t kb = wave + 16 * i;
+        if (kb >= nkb) continue;
+        uint2 c[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {   // 8 elements each
+            float v[8];
+            if constexpr (sizeof(InT) == 2) {
+                unpack8(d[i][h], v);
+            } else {
+                const uint4 a = d[i][2 * h], b = d[i][2 * h + 1];
+                v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z);
+                v[3] = __uint_as_float(a.w); v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+                v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+            }
+            c[h] = encode_chunk_dynamic<InT>(v, p);
+        }
+        uint8_t* blk = q + (((int64_t)blockIdx.x * nkb + kb) << 11) + (lane << 4);
+        store16_stream(blk, make_uint4(c[0].x, c[0].y, c[1].x, c[1].y));
+        store16_stream(blk + 1024, make_uint4(c[2].x, c[2].y, c[3].x, c[3].y));
+    }
+}
+
+// The tile kernel holds 32 elements per k block per lane in at most 128
+// registers (16 waves per workgroup): up to 4 k blocks per wave for bf16
+// (K <= 8192), 2 for fp32 (K <= 4096).
+bool row_quant_tiles_fit(bool x_is_bf16, int64_t K) {
+    return K > 0 && K % 128 == 0 && K <= (x_is_bf16 ? 8192 : 4096);
+}
+
+hipError_t launch_row_quant_tiles(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
+                                  hipStream_t stream) {
+    if (M == 0) return hipSuccess;
+    if (!row_quant_tiles_fit(x_is_bf16, K)) return hipErrorInvalidValue;
+    const int64_t per = (K / 128 + 15) / 16;   // k blocks per wave
+    const dim3 grid((unsigned)((M + 15) / 16)), block(1024);
+    if (x_is_bf16) {
+        const uint16_t* xb = (const uint16_t*)x;
+        if (per <= 1) row_quant_tile16<uint16_t, 1><<<grid, block, 0, stream>>>(xb, M, K, q, scales);
+        else if (per <= 2) row_quant_tile16<uint16_t, 2><<<grid, block, 0, stream>>>(xb, M, K, q, scales);
+        else row_quant_tile16<uint16_t, 4><<<grid, block, 0, stream>>>(xb, M, K, q, scales);
+    } else {
+        const float* xf = (const float*)x;
+        if (per <= 1) row_quant_tile16<float, 1><<<grid, block, 0, stream>>>(xf, M, K, q, scales);
+        else row_quant_tile16<float, 2><<<grid, block, 0, stream>>>(xf, M, K, q, scales);
+    }
+    return hipGetLastError();
+}
+
 template <typename InT, bool kPacked>
 static hipError_t launch_row_quant_t(const InT* x, int64_t M, int64_t K, uint8_t* q, float* scales,
                                      hipStream_t stream) {

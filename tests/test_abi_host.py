@@ -147,8 +147,9 @@ def test_gemm_validation(lib):
     assert call(y=A + 4) == b.E_ALIGN
     assert call(M=0) == b.OK
     # a bf16 activation needs the workspace the size query reports: the codes
-    # (fragment order, rows padded to 16, for M <= 32 and for every per-tensor
-    # scale; per-token rows above 32 row-major), then
+    # (fragment order, rows padded to 16, for M <= 32, for every per-tensor
+    # scale and for per-token rows when K <= 8192 bf16 / 4096 fp32; other
+    # per-token rows above 32 row-major), then
     # the per-token scales -- except bf16 per-token with M <= 4 and K <= 4096,
     # which the decode kernel quantizes itself (no workspace)
     assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4, 8, 128) == 0
@@ -163,7 +164,12 @@ def test_gemm_validation(lib):
     assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TENSOR, 17, 8, 256) == 32 * 256
     assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TENSOR, 33, 8, 256) == 48 * 256
     assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TENSOR, 4096, 8, 8192) == 4096 * 8192
-    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 33, 8, 128) == 4352 + 256  # 33 * 128 rounded up to 256
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 33, 8, 128) == 48 * 128 + 256
+    al = lambda v: (v + 255) // 256 * 256
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4100, 8, 8192) == al(4112 * 8192) + al(4100 * 4)
+    # past the tile quantizer's register budget: row-major codes
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 33, 8, 8320) == al(33 * 8320) + al(33 * 4)
+    assert lib.fp8_scaled_gemm_workspace_size(b.F32, b.SCALE_PER_TOKEN, 33, 8, 4224) == al(33 * 4224) + al(33 * 4)
     assert call(a_dt=b.BF16, sa=None, M=12) == b.E_WORKSPACE
     assert call(a_dt=b.BF16, sa=None, M=12, ws=A, wsb=need - 1) == b.E_WORKSPACE
     assert call(a_dt=b.BF16, sa=None, M=12, ws=A + 16, wsb=need) == b.E_ALIGN
@@ -399,8 +405,10 @@ def test_noalloc_gemm_validation(lib):
     workspace would exceed the static scratch is refused before any HIP call."""
     g = lib.fp8_scaled_gemm_noalloc
     cap = b.SCRATCH_BYTES
-    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4092, 8, 4096) == cap
-    assert g(A, b.BF16, None, b.SCALE_PER_TOKEN, A, 0, A, A, b.BF16, 4093, 8, 4096, b.ACCUM_EXACT,
+    # bf16 per-token codes in the fragment order (rows padded to 16) + the scales: 4080 rows fit, 4081 do not
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4080, 8, 4096) <= cap
+    assert lib.fp8_scaled_gemm_workspace_size(b.BF16, b.SCALE_PER_TOKEN, 4081, 8, 4096) > cap
+    assert g(A, b.BF16, None, b.SCALE_PER_TOKEN, A, 0, A, A, b.BF16, 4081, 8, 4096, b.ACCUM_EXACT,
              None) == b.E_SCRATCH
     assert g(A, b.F32, A, b.SCALE_PER_TENSOR, A, 0, A, A, b.BF16, 8193, 8, 2048, b.ACCUM_EXACT,
              None) == b.E_SCRATCH

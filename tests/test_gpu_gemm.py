@@ -235,6 +235,47 @@ def test_decode_static_scale_in_call(m, n, k, accum, layout):
                   what=f"decode static {m}x{n}x{k} s={s!r} {accum} {layout}")
 
 
+@pytest.mark.parametrize("m,k,dt", [(33, 128, "bf16"), (129, 8192, "bf16"), (300, 1024, "bf16"), (50, 4096, "f32"),
+                                    (1000, 2944, "bf16"), (40, 8320, "bf16")])
+def test_per_token_codes_in_the_call_workspace(m, k, dt):
+    """The codes and scales a per-token call leaves in its workspace against the
+    oracle's per-token quantizer, byte for byte on every live row: the fragment
+    order (rows padded to 16) written by the 16-row-tile quantizer where its
+    registers hold a tile's rows (bf16 K <= 8192, fp32 K <= 4096), row-major
+    codes beyond that (K = 8320); the scales follow at the next 256 bytes."""
+    from test_abi_host import pack_reference
+    from workloads import bf16_bits_from_f32
+    rng = np.random.default_rng(m * 13 + k)
+    x = (rng.standard_t(3, (m, k)) * 2).astype(np.float32)
+    x[rng.integers(0, m, 3)] = 0.0                      # zero rows: unit scales
+    x[:, rng.integers(0, k, 2)] *= 30
+    if dt == "bf16":
+        xb = bf16_bits_from_f32(x)
+        xt, xf = dev_bf16(xb), f32_from_bf16_bits(xb)
+    else:
+        xt, xf = dev(x), x
+    n = 16
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    wq_t, sw_t = sg.fp8_quant_weight_per_channel(dev(w))
+    nbytes = sg.fp8_scaled_gemm_workspace_size(xt.dtype, "per_token", m, n, k)
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    sg.fp8_scaled_gemm(xt, None, wq_t, sw_t, workspace=ws)
+    torch.cuda.synchronize()
+    wsh = host(ws)
+    want_q, want_s = w8a8.quant_per_token(xf)
+    packed = k <= (8192 if dt == "bf16" else 4096)
+    rows = (m + 15) // 16 * 16 if packed else m
+    codes = wsh[:rows * k]
+    if packed:
+        live = pack_reference(np.ones((m, k), np.uint8)).astype(bool)
+        assert_codes_equal(codes[live], pack_reference(want_q)[live], f"{m}x{k} {dt} packed codes")
+    else:
+        assert_codes_equal(codes.reshape(m, k), want_q, f"{m}x{k} {dt} row-major codes")
+    off = (rows * k + 255) // 256 * 256
+    got_s = wsh[off:off + 4 * m].view(np.float32)
+    assert np.array_equal(got_s.view(np.uint32), np.asarray(want_s, np.float32).view(np.uint32)), f"{m}x{k} {dt} scales"
+
+
 def _sample(M, N, seed, nr=40, nc=384, tile=256):
     """Rows and columns to compare at full size: the first and last, one at random
     inside every 256-row and every 256-column tile (so every output tile of the
