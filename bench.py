@@ -713,6 +713,11 @@ def run_details(sg, torch, dev, to_bf16, T, wanted, clock):
                                                                   a_scale_layout="kmajor"), min_calls=50)
             out.append(tflops_row(f"block-wise prefill GEMM {M}x{N}x{K} (k-block-major activation scales)", d,
                                   2.0 * M * N * K, "mfma_fp8"))
+            d = T.per_call(lambda i: sg.fp8_scaled_gemm_blockwise(aq, sa, wp, sw, y=y, accum="exact",
+                                                                  w_layout="packed", w_shape=(N, K),
+                                                                  a_scale_layout="kmajor"), min_calls=50)
+            out.append(tflops_row(f"block-wise prefill GEMM {M}x{N}x{K} exact partials (k-block-major activation "
+                                  f"scales)", d, 2.0 * M * N * K, "exact"))
             aq2, sa2 = sg.fp8_quant_per_token_group(xl[0])
             d = T.per_call(lambda i: sg.fp8_scaled_gemm_blockwise(aq2, sa2, wp, sw, y=y, accum="mfma_fp8",
                                                                   w_layout="packed", w_shape=(N, K)), min_calls=50)

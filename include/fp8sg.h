@@ -336,8 +336,8 @@ fp8sg_status fp8_quant_weight_blockwise(const void* w, int w_dtype, int64_t N, i
  *   layout    0 or an OR of FP8SG_W_PACKED, FP8SG_A_PACKED and FP8SG_SCALES_KMAJOR
  *   accum     FP8SG_ACCUM_MFMA_FP8: each P_g is one FP8 matrix-core product
  *             (with that hardware's in-instruction alignment, see fp8sg_accum);
- *             FP8SG_ACCUM_EXACT: P_g formed exactly on the bf16 matrix cores,
- *             available for M <= 32 only (larger M: FP8SG_E_DTYPE).
+ *             FP8SG_ACCUM_EXACT: P_g formed exactly on the bf16 matrix cores
+ *             (every M).
  *   K % 128 == 0 and K < 2^24; M, N >= 0 arbitrary.
  */
 fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales, const uint8_t* wq, int layout,

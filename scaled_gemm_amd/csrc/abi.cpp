@@ -346,7 +346,6 @@ fp8sg_status fp8_scaled_gemm_blockwise(const uint8_t* a_q, const float* a_scales
     if ((layout & ~(FP8SG_W_PACKED | FP8SG_A_PACKED | FP8SG_SCALES_KMAJOR)) != 0) return FP8SG_E_DTYPE;
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxGemmK) return FP8SG_E_SHAPE;
     if (K % 128 != 0) return FP8SG_E_SHAPE;
-    if (accum == FP8SG_ACCUM_EXACT && M > 32) return FP8SG_E_DTYPE;  // exact partials: skinny kernel only
     if (M == 0 || N == 0) return FP8SG_OK;
     if (!y) return FP8SG_E_NULL;
     if (K > 0 && (!a_q || !wq || !a_scales || !w_scales)) return FP8SG_E_NULL;

@@ -52,10 +52,8 @@ hipError_t launch_gemm_blockwise(const uint8_t* aq, bool a_packed, const float* 
     if (M <= 32)
         return launch_skinny_blockwise(aq, a_packed, a_scales, sa_kmajor, wq, w_packed, w_scales, y, y_bf16, m, n, k,
                                        fp8_mfma, stream);
-    // exact block-wise accumulation exists for M <= 32 only (checked by the ABI)
-    if (!fp8_mfma) return hipErrorInvalidValue;
     return launch_big_blockwise(aq, a_packed, a_scales, sa_kmajor, wq, w_packed, w_scales, y, y_bf16, m, n, k,
-                                stream);
+                                fp8_mfma, stream);
 }
 
 // ---------------------------------------------------------------------------

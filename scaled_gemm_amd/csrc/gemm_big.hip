@@ -619,6 +619,296 @@ __global__ __launch_bounds__(512, 1) void gemm_big_blockwise(const uint8_t* __re
 static_assert(8 * (kEpiWaveBytes / 2) <= 2 * kBwStage, "the staged output reuses the two operand stages");
 
 // ---------------------------------------------------------------------------
+// Block-wise scaled GEMM for M > 32 with exact partials: each 128-deep partial
+// P_kb is formed on the bf16 matrix cores from the exactly widened codes (as in
+// gemm_big_exact), then multiplied by its scale product and added to an fp32
+// accumulator with vector FMAs (the same promotion as gemm_big_blockwise).  The
+// FMAs read the partials and write the accumulators, so both live in the
+// vector registers: a wave owns 64 x 64 outputs, 4 partials and 4 accumulators
+// of 32 x 32 (128 registers), and two waves share each SIMD.
+//
+// 256 (m) x 128 (n) tile per workgroup of 8 waves.  Wave (wm, wn) = (wave % 4,
+// wave / 4) owns tile rows 64 wm .. 64 wm + 63 (A fragments 2 wm, 2 wm + 1)
+// and columns 64 wn .. 64 wn + 63 (W fragments 2 wn, 2 wn + 1); fragment and
+// output lane layouts as in gemm_big_exact.  Half-block slots as there: the
+// copies run four half blocks ahead, the next half block's fragments are read
+// during the first two steps of the current one, and each slot holds the 16 A
+// subtiles (16 KB), the 8 W subtiles (8 KB) and, in the slot of a k block's
+// first half, the block's scales.  Per half block every wave copies A subtiles
+// 2 w and 2 w + 1 and W subtile w; in a k block's first half also one
+// 4-byte-per-lane copy of scales: waves 0-3 the s_a of tile rows 64 w + lane,
+// waves 4-7 the tile's s_w (one value in every lane; each of these waves makes
+// its own copy, so that every wave has the same number of copies in flight).
+// A k block's scales are read with its first half block's fragments, before
+// the barrier that lets that slot be refilled.
+constexpr int kBxTileN = 128;
+constexpr int kBxOps = 24 * 1024;          // A 16 KB + W 8 KB
+constexpr int kBxSlot = kBxOps + 2048;     // + s_a (256 floats) + 4 copies of s_w (64 floats each)
+constexpr int kBxSlots = 4;
+constexpr int kBxEpiWaveBytes = 64 * 128;  // a wave's 64 x 64 bf16 outputs, staged
+static_assert(8 * kBxEpiWaveBytes <= kBxSlots * kBxSlot, "the staged output reuses the slots");
+
+template <int kOut, bool kWPacked, bool kAPacked>
+__global__ __launch_bounds__(512, 1) void gemm_big_blockwise_exact(const uint8_t* __restrict__ A,
+                                                                   const float* __restrict__ sa, int sa_kmajor,
+                                                                   const uint8_t* __restrict__ W,
+                                                                   const float* __restrict__ sw,
+                                                                   void* __restrict__ Y, int M, int N, int K,
+                                                                   int tiles_per_xcd) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // kBxSlots x kBxSlot
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 3, wn = wave >> 2;
+    int tile;
+    int64_t m_base, n_base;
+    tile_coords<kBxTileN>(M, N, tiles_per_xcd, tile, m_base, n_base);
+    if (tile < 0) return;
+    const int nkb = K >> 7;
+    const int nhb = 2 * nkb;
+
+    f32x16 acc[2][2], p[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // copy c = 0, 1: A subtile 2 wave + c; c = 2: W subtile wave.  o[c]: the lane's
+    // source offset at k block 0, half 0, relative to the tile's first row.
+    uint32_t o[3];
+    {
+        const int r16 = lane & 15, kq = (lane >> 4) * 32;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            const bool is_a = c < 2;
+            const int sub = is_a ? 2 * wave + c : wave;
+            const bool packed = is_a ? kAPacked : kWPacked;
+            const int64_t base_row = is_a ? m_base : n_base;
+            const int rows = is_a ? M : N;
+            if (packed) {
+                int64_t t = (base_row >> 4) + sub;
+                const int64_t last_tile = ((int64_t)rows + 15) / 16 - 1;
+                t = t < last_tile ? t : last_tile;
+                o[c] = (uint32_t)((t - (base_row >> 4)) * (int64_t)nkb * kPackBlock + 16 * lane);
+            } else {
+                int64_t r = base_row + 16 * sub + r16;
+                r = r < rows ? r : rows - 1;
+                o[c] = (uint32_t)((r - base_row) * K + kq);
+            }
+        }
+    }
+    const uint8_t* a_src = kAPacked ? A + (m_base >> 4) * (int64_t)nkb * kPackBlock : A + m_base * K;
+    const uint8_t* w_src = kWPacked ? W + (n_base >> 4) * (int64_t)nkb * kPackBlock : W + n_base * K;
+    const int64_t a_kb = kAPacked ? kPackBlock : 128, a_h = kAPacked ? 1024 : 16;
+    const int64_t w_kb = kWPacked ? kPackBlock : 128, w_h = kWPacked ? 1024 : 16;
+    // the scale this lane copies: s_a of tile row 64 wave + lane (waves 0-3) or the
+    // tile's s_w (waves 4-7); s_a [M, K/128] row-major or k-block-major [K/128, M]
+    const float* ssrc;
+    int64_t sstep = 1;
+    if (wave < 4) {
+        int64_t m = m_base + 64 * wave + lane;
+        m = m < M ? m : M - 1;
+        ssrc = sa_kmajor ? sa + m : sa + m * nkb;
+        sstep = sa_kmajor ? (int64_t)M : 1;
+    } else {
+        const int64_t nbw = ((int64_t)N + 127) >> 7;
+        int64_t nb = n_base >> 7;
+        nb = nb < nbw ? nb : nbw - 1;
+        ssrc = sw + nb * nkb;
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    const uint32_t dst_a = lds0 + (uint32_t)(2 * wave) * 1024u;
+    const uint32_t dst_w = lds0 + 16 * 1024u + (uint32_t)wave * 1024u;
+    const uint32_t dst_s = lds0 + (uint32_t)kBxOps + 256u * (uint32_t)wave;
+
+    // copy c of half block hb (clamped to the last one) into slot hb % 4; the
+    // scale copy of the k block whose first half hb is (hb even)
+    auto copy = [&](int c, int hb) __attribute__((always_inline)) {
+        const uint32_t slot = (uint32_t)((hb & (kBxSlots - 1)) * kBxSlot);
+        hb = hb < nhb ? hb : nhb - 1;
+        if (c < 2)
+            copy16_to_lds(a_src + (int64_t)(hb >> 1) * a_kb + (int64_t)(hb & 1) * a_h + o[c],
+                          dst_a + slot + (uint32_t)c * 1024u);
+        else
+            copy16_to_lds(w_src + (int64_t)(hb >> 1) * w_kb + (int64_t)(hb & 1) * w_h + o[2], dst_w + slot);
+    };
+    auto copy_scales = [&](int hb) __attribute__((always_inline)) {
+        const uint32_t slot = (uint32_t)((hb & (kBxSlots - 1)) * kBxSlot);
+        int kb = hb >> 1;
+        kb = kb < nkb ? kb : nkb - 1;
+        copy4_to_lds(ssrc + (int64_t)kb * sstep, dst_s + slot);
+    };
+
+    // Fragment reads: t = 0, 1 the wave's W fragments, t = 2, 3 its A fragments;
+    // slot part u (0, 1): the lane's 16 bytes of the half block.
+    const int lane_off = ((lane & 31) >> 4) * 1024 + (lane & 15) * 16 + (lane >> 5) * 512;
+    const uint8_t* rd_w = smem + 16 * 1024 + wn * 4 * 1024 + lane_off;
+    const uint8_t* rd_a = smem + wm * 4 * 1024 + lane_off;
+    uint4 raw[2][4][2];
+    auto read = [&](int b, int t, int u, int hb) __attribute__((always_inline)) {
+        const int slot = (hb & (kBxSlots - 1)) * kBxSlot;
+        const uint8_t* q = (t < 2 ? rd_w + 2048 * t : rd_a + 2048 * (t - 2)) + slot + 256 * u;
+        raw[b][t][u] = *reinterpret_cast<const uint4*>(q);
+    };
+    // scales of the k block whose first half is hb: s_a of the lane's two rows, s_w
+    float nsa[2], nsw;
+    auto read_scales = [&](int hb) __attribute__((always_inline)) {
+        const float* ls = reinterpret_cast<const float*>(smem + (hb & (kBxSlots - 1)) * kBxSlot + kBxOps);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) nsa[j] = ls[64 * wm + 32 * j + (lane & 31)];
+        nsw = ls[256];
+    };
+    bf16x8 v[2][4];
+    auto widen = [&](int vb, int b, int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const uint4 r = raw[b][f][t >> 1];
+            v[vb][f] = (t & 1) ? widen8(r.z, r.w) : widen8(r.x, r.y);
+        }
+    };
+
+    if (nhb > 0) {
+#pragma unroll
+        for (int h = 0; h < kBxSlots; ++h) {
+#pragma unroll
+            for (int c = 0; c < 3; ++c) copy(c, h);
+            if ((h & 1) == 0) copy_scales(h);
+        }
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(10));   // this wave's copies of half block 0 have landed
+        barrier_no_fence();                           // ... and every other wave's
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) read(0, t, u, 0);
+        read_scales(0);
+        widen(0, 0, 0);
+    }
+
+    float f[2] = {0.0f, 0.0f};
+    // Half block hb (b = hb % 2), its fragments in raw[b]: four steps of 16 k.
+    // Steps 0-2 issue the three operand copies of hb + 4 (step 3 the scale copy
+    // when hb + 4 starts a k block); steps 0 and 1 read hb + 1 into raw[b ^ 1]
+    // (and, when hb + 1 starts a k block, its scales); each step widens the next
+    // step's operands between its multiplies.  The first step of a k block starts
+    // the partials from zero; after the last one they are promoted.
+    auto half_block = [&](int hb, int b) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        // copies in flight after this wait: those of hb + 2 and hb + 3 (3 + 4 in some order)
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(7));
+        barrier_no_fence();
+        if (b == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) f[j] = nsa[j] * nsw;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (t < 3) copy(t, hb + 4);
+            else if (b == 0) copy_scales(hb + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            if (b == 1 && t == 1) read_scales(hb + 1);
+            if (t < 2) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) read(b ^ 1, 2 * t + q, u, hb + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const f32x16 c = (b == 0 && t == 0) ? f32x16{} : p[i][j];
+                    p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[t & 1][i], v[t & 1][2 + j], c, 0, 0, 0);
+                }
+            if (t < 3) widen((t + 1) & 1, b, t + 1);
+            else widen(0, b ^ 1, 0);
+            // issue order: each multiply followed by four converts (the reads first, one per multiply)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (t < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (b == 1) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[i][j][r], f[j], acc[i][j][r]);
+        }
+    };
+
+    for (int hb = 0; hb < nhb; hb += 2) {
+        half_block(hb, 0);
+        half_block(hb + 1, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // no copy into LDS may outlive the workgroup
+
+    static_assert(kOut == kOutBF16 || kOut == kOutF32, "block-wise GEMMs write bf16 or fp32");
+    if (kOut == kOutBF16) {
+        // stage the wave's 64 x 64 outputs row-major (128-byte rows, 16-byte slots
+        // XORed with the row's low three bits), then store 16 bytes per lane
+        __syncthreads();  // every wave is done with the slots
+        uint8_t* wl = smem + wave * kBxEpiWaveBytes;
+        auto off = [](int row, int col_bytes) { return row * 128 + (col_bytes ^ ((row & 7) << 4)); };
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int row = 32 * j + (lane & 31);
+                    const int col = 32 * i + 8 * g + 4 * (lane >> 5);
+                    uint2 w2;
+                    w2.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+                    w2.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    *reinterpret_cast<uint2*>(wl + off(row, 2 * col)) = w2;
+                }
+        __syncthreads();
+        const int c = lane & 7;
+        const int64_t n = n_base + 64 * wn + 8 * c;
+        const bool vec = (N & 7) == 0 && n + 8 <= N;
+        uint16_t* Yb = (uint16_t*)Y;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int row = 8 * it + (lane >> 3);
+            const int64_t m = m_base + 64 * wm + row;
+            if (m >= M) continue;
+            const uint4 val = *reinterpret_cast<const uint4*>(wl + off(row, 16 * c));
+            uint16_t* yr = Yb + m * N;
+            if (vec) {
+                *reinterpret_cast<uint4*>(yr + n) = val;
+            } else {
+                const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) yr[n + e] = (uint16_t)((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            }
+        }
+        return;
+    }
+    const bool vec_ok = (N & 3) == 0;
+    const QScale q = out_qscale<kOut>(nullptr);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t m = m_base + 64 * wm + 32 * j + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n0 = n_base + 64 * wn + 32 * i + 8 * g + 4 * (lane >> 5);
+                const f32x4 a = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                if (n0 < N) store4_raw<kOut>(Y, N, m, n0, a, vec_ok, q);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers: tiles_per_xcd tiles for each of the 8 XCDs (tile_coords).
 template <bool kFp8, int kOut, bool kWPacked, bool kAPacked>
 static hipError_t launch_big_t(const uint8_t* aq, const float* sa, int sa_pt, const uint8_t* wq, const float* sw,
@@ -668,20 +958,28 @@ hipError_t launch_big_gemm(const uint8_t* aq, bool a_packed, const float* sa, in
 
 template <int kOut, bool kWPacked, bool kAPacked>
 static hipError_t launch_big_bw_t(const uint8_t* aq, const float* sa, int sa_kmajor, const uint8_t* wq,
-                                  const float* sw, void* y, int M, int N, int K, hipStream_t stream) {
-    const int tiles = ((M + kBig - 1) / kBig) * ((N + kBig - 1) / kBig);
-    const int per = (tiles + 7) / 8;
-    gemm_big_blockwise<kOut, kWPacked, kAPacked><<<dim3((unsigned)(per * 8)), dim3(512), 2 * kBwStage, stream>>>(
-        aq, sa, sa_kmajor, wq, sw, y, M, N, K, per, nullptr);
+                                  const float* sw, void* y, int M, int N, int K, bool fp8_mfma, hipStream_t stream) {
+    if (fp8_mfma) {
+        const int tiles = ((M + kBig - 1) / kBig) * ((N + kBig - 1) / kBig);
+        const int per = (tiles + 7) / 8;
+        gemm_big_blockwise<kOut, kWPacked, kAPacked><<<dim3((unsigned)(per * 8)), dim3(512), 2 * kBwStage, stream>>>(
+            aq, sa, sa_kmajor, wq, sw, y, M, N, K, per, nullptr);
+    } else {
+        const int tiles = ((M + kBig - 1) / kBig) * ((N + kBxTileN - 1) / kBxTileN);
+        const int per = (tiles + 7) / 8;
+        gemm_big_blockwise_exact<kOut, kWPacked, kAPacked>
+            <<<dim3((unsigned)(per * 8)), dim3(512), kBxSlots * kBxSlot, stream>>>(aq, sa, sa_kmajor, wq, sw, y, M,
+                                                                                  N, K, per);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_big_blockwise(const uint8_t* aq, bool a_packed, const float* sa, bool sa_kmajor, const uint8_t* wq,
                                 bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
-                                hipStream_t stream) {
+                                bool fp8_mfma, hipStream_t stream) {
     const int km = sa_kmajor ? 1 : 0;
 #define FP8SG_BW(YB, WP, AP) \
-    launch_big_bw_t<(YB) ? kOutBF16 : kOutF32, WP, AP>(aq, sa, km, wq, sw, y, M, N, K, stream)
+    launch_big_bw_t<(YB) ? kOutBF16 : kOutF32, WP, AP>(aq, sa, km, wq, sw, y, M, N, K, fp8_mfma, stream)
     if (y_bf16) {
         if (a_packed) return w_packed ? FP8SG_BW(true, true, true) : FP8SG_BW(true, false, true);
         return w_packed ? FP8SG_BW(true, true, false) : FP8SG_BW(true, false, false);

@@ -22,7 +22,7 @@ hipError_t launch_big_gemm(const uint8_t* aq, bool a_packed, const float* sa, in
                            int K, bool fp8_mfma, hipStream_t stream);
 hipError_t launch_big_blockwise(const uint8_t* aq, bool a_packed, const float* sa, bool sa_kmajor, const uint8_t* wq,
                                 bool w_packed, const float* sw, void* y, bool y_bf16, int M, int N, int K,
-                                hipStream_t stream);
+                                bool fp8_mfma, hipStream_t stream);
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -275,9 +275,12 @@ __device__ __forceinline__ void issue_stage_copy(int i, uint8_t* __restrict__ st
         copy16_to_lds(w_tile + w_off + ow[k], lds_base + (uint32_t)((16 + j) * kPackBlock + h * 1024));
 }
 
+// Tile of workgroup blockIdx.x: 256 (m) x kTileN (n) tiles, tiles_per_xcd of them
+// on each of the 8 XCDs (consecutive workgroups go to consecutive XCDs).
+template <int kTileN = kBig>
 __device__ __forceinline__ void tile_coords(int M, int N, int tiles_per_xcd, int& tile, int64_t& m_base,
                                             int64_t& n_base) {
-    const int tiles_n = (N + kBig - 1) / kBig;
+    const int tiles_n = (N + kTileN - 1) / kTileN;
     const int tiles = ((M + kBig - 1) / kBig) * tiles_n;
     tile = (int)(blockIdx.x & 7) * tiles_per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= tiles) {
@@ -292,7 +295,7 @@ __device__ __forceinline__ void tile_coords(int M, int N, int tiles_per_xcd, int
     const int gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
     const int t = tile % grp;
     m_base = (int64_t)(first_m + t % gm) * kBig;
-    n_base = (int64_t)(t / gm) * kBig;
+    n_base = (int64_t)(t / gm) * kTileN;
 }
 
 // Workgroup barrier without a memory fence.  __syncthreads() also orders

@@ -336,7 +336,7 @@ def fp8_scaled_gemm_blockwise(a: torch.Tensor, a_scales: torch.Tensor, wq: torch
 
     a: E4M3 codes [M, K] (or the packed 1-D buffer with a_shape=(M, K));
     a_scales [M, K/128]; wq [N, K] (or packed with w_shape=(N, K));
-    w_scales [ceil(N/128), K/128].  accum="exact" needs M <= 32.
+    w_scales [ceil(N/128), K/128].  accum: "mfma_fp8" or "exact".
     a_scale_layout="kmajor": a_scales is [K/128, M]."""
     _need(a, "a", (torch.uint8,))
     _need(wq, "wq", (torch.uint8,))

@@ -65,9 +65,11 @@ def test_blockwise_validation(lib):
     assert lib.fp8_quant_weight_blockwise(A, b.E5M2, 4, 128, A, A, None) == b.E_DTYPE
     assert lib.fp8_quant_weight_blockwise(A, b.F32, 4, 128, None, A, None) == b.E_NULL
     assert lib.fp8_quant_weight_blockwise(None, b.F32, 0, 128, None, None, None) == b.OK
-    # GEMM: exact accumulation only for M <= 32; K % 128; layout bits; nulls; alignment
+    # GEMM: accumulation mode; K % 128; layout bits; nulls; alignment
     g = lib.fp8_scaled_gemm_blockwise
-    assert g(A, A, A, 0, A, A, b.BF16, 33, 8, 128, b.ACCUM_EXACT, None) == b.E_DTYPE
+    assert g(A, A, A, 0, A, A, b.BF16, 33, 8, 128, 7, None) == b.E_DTYPE
+    # exact accumulation at every M (an empty call succeeds without a device)
+    assert g(None, None, None, 0, None, None, b.BF16, 0, 8, 128, b.ACCUM_EXACT, None) == b.OK
     assert g(A, A, A, 0, A, A, b.BF16, 4, 8, 100, b.ACCUM_MFMA_FP8, None) == b.E_SHAPE
     assert g(A, A, A, 4, A, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_DTYPE
     assert g(A, A, A, 16, A, A, b.BF16, 4, 8, 128, b.ACCUM_MFMA_FP8, None) == b.E_DTYPE

@@ -5,7 +5,7 @@ the C ABI.
 Quantizers: codes and scales bit-exact.
 
 GEMM, y = sum_g s_a[m, g] s_w[n // 128, g] P_g (read through the fp32 output):
-  * exact mode (bf16 matrix cores, M <= 32): |y - y_exact| <= 1e-5 * T, with
+  * exact mode (bf16 matrix cores, every M): |y - y_exact| <= 1e-5 * T, with
     T = sum_g |s_a s_w| sum_{k in g} |a_k w_k| -- the accumulator tolerance of
     the per-token GEMM applied to the block-scaled terms;
   * FP8 matrix-core mode: the bound derived from that hardware's summation
@@ -180,19 +180,19 @@ def test_ragged(m, n, k, layout, kmajor):
         x[m // 2, 128:256] = 0.0                                     # an all-zero group (scale 1.0)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     w[: min(n, 128), :128] *= 30                                     # one block with larger weights
-    accums = ["mfma_fp8", "exact"] if m <= 32 else ["mfma_fp8"]
-    for accum in accums:
+    for accum in ("mfma_fp8", "exact"):
         run_case(bf16_bits_from_f32(x), w, accum=accum, w_layout=layout, a_layout=layout, kmajor=kmajor,
                  what=f"ragged {m}x{n}x{k} {accum} {layout} kmajor={kmajor}")
 
 
+@pytest.mark.parametrize("accum", ["mfma_fp8", "exact"])
 @pytest.mark.parametrize("kmajor", [False, True], ids=["scales_row_major", "scales_kmajor"])
 @pytest.mark.parametrize("k", [4096, 14336])
-def test_prefill_sampled(k, kmajor):
+def test_prefill_sampled(k, kmajor, accum):
     xb, w, _ = prefill_inputs(k)
     rows, cols = _sample(xb.shape[0], w.shape[0], k)
-    run_case(xb, w, accum="mfma_fp8", rows=rows, cols=cols, w_layout="packed", a_layout="row_major",
-             what=f"prefill K={k} kmajor={kmajor}", kmajor=kmajor)
+    run_case(xb, w, accum=accum, rows=rows, cols=cols, w_layout="packed", a_layout="row_major",
+             what=f"prefill K={k} kmajor={kmajor} {accum}", kmajor=kmajor)
 
 
 def test_fp32_input_and_packed_codes():
@@ -218,15 +218,50 @@ def test_deterministic_repeats():
     wq, sw = sg.fp8_quant_weight_blockwise(dev(w))
     outs = [host_bits16(sg.fp8_scaled_gemm_blockwise(aq, sa, wq, sw)) for _ in range(8)]
     small = [host_bits16(sg.fp8_scaled_gemm_blockwise(aq[:24], sa[:24], wq, sw, accum=a)) for a in ("exact",) * 4]
+    exact = [host_bits16(sg.fp8_scaled_gemm_blockwise(aq, sa, wq, sw, accum="exact")) for _ in range(4)]
     assert all(np.array_equal(o, outs[0]) for o in outs)
     assert all(np.array_equal(o, small[0]) for o in small)
+    assert all(np.array_equal(o, exact[0]) for o in exact)
 
 
-def test_exact_mode_refuses_large_m():
-    aq = torch.zeros((33, 128), dtype=torch.uint8, device="cuda")
-    sa = torch.ones((33, 1), dtype=torch.float32, device="cuda")
-    wq = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
-    sw = torch.ones((1, 1), dtype=torch.float32, device="cuda")
-    with pytest.raises(sg.Fp8sgError) as e:
-        sg.fp8_scaled_gemm_blockwise(aq, sa, wq, sw, accum="exact")
-    assert e.value.status == sg.fp8sg.E_DTYPE
+@pytest.mark.parametrize("m,n,k", [(600, 700, 1024), (257, 129, 384), (33, 4100, 256)])
+def test_exact_layouts_agree_bit_for_bit(m, n, k):
+    """Exact mode sums each block's products in one fixed k order whatever the
+    operand layouts: row-major or packed A and W, row-major or k-block-major
+    activation scales give the same bits, and so do repeated calls."""
+    rng = np.random.default_rng(m + n + k)
+    x = bf16_bits_from_f32(rng.standard_normal((m, k)).astype(np.float32) * 3)
+    w = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    aq, sa = sg.fp8_quant_per_token_group(dev_bf16(x))
+    sa_km = sa.t().contiguous()
+    wq, sw = sg.fp8_quant_weight_blockwise(dev(w))
+    ap, wp = sg.fp8_pack_weights(aq), sg.fp8_pack_weights(wq)
+    outs = []
+    for a_in, al in ((aq, "row_major"), (ap, "packed")):
+        for w_in, wl in ((wq, "row_major"), (wp, "packed")):
+            for s_in, sl in ((sa, "row_major"), (sa_km, "kmajor")):
+                for dt in (torch.float32, torch.bfloat16):
+                    y = sg.fp8_scaled_gemm_blockwise(a_in, s_in, w_in, sw, accum="exact", out_dtype=dt, a_layout=al,
+                                                     w_layout=wl, a_shape=(m, k), w_shape=(n, k), a_scale_layout=sl)
+                    outs.append((dt, host(y.view(torch.int32) if dt == torch.float32 else y.view(torch.int16))))
+    again = host(sg.fp8_scaled_gemm_blockwise(aq, sa, wq, sw, accum="exact", out_dtype=torch.float32)
+                 .view(torch.int32))
+    torch.cuda.synchronize()
+    f32 = [o for dt, o in outs if dt == torch.float32]
+    b16 = [o for dt, o in outs if dt == torch.bfloat16]
+    assert all(np.array_equal(o, f32[0]) for o in f32) and np.array_equal(again, f32[0])
+    assert all(np.array_equal(o, b16[0]) for o in b16)
+
+
+@pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
+def test_empty_k_writes_zeros(accum):
+    """K = 0: every output is the empty sum, 0, at a large-tile M."""
+    aq = torch.zeros((300, 0), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((300, 0), dtype=torch.float32, device="cuda")
+    wq = torch.zeros((200, 0), dtype=torch.uint8, device="cuda")
+    sw = torch.zeros((2, 0), dtype=torch.float32, device="cuda")
+    for dt in (torch.float32, torch.bfloat16):
+        y = torch.full((300, 200), float("nan"), dtype=dt, device="cuda")
+        sg.fp8_scaled_gemm_blockwise(aq, sa, wq, sw, accum=accum, out_dtype=dt, y=y)
+        torch.cuda.synchronize()
+        assert bool((y == 0).all()), f"K = 0 {accum} {dt}"
