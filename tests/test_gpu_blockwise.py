@@ -141,12 +141,13 @@ def run_case(x, w, *, accum, rows=None, cols=None, w_layout="row_major", a_layou
                cols, accum, what)
 
 
-def _sample(M, N, seed, nr=24, nc=256, tile=256):
+def _sample(M, N, seed, nr=24, nc=256, tile=256, tile_n=128):
     """First and last rows / columns, one at random inside every 256-row and
-    256-column tile (every output tile of the large-tile kernel), and more at random."""
+    128-column tile (every output tile of both large-tile kernels: 256 x 256 in
+    FP8 mode, 256 x 128 in exact mode), and more at random."""
     rng = np.random.default_rng(seed)
     per_r = [rng.integers(t, min(t + tile, M)) for t in range(0, M, tile)]
-    per_c = [rng.integers(t, min(t + tile, N)) for t in range(0, N, tile)]
+    per_c = [rng.integers(t, min(t + tile_n, N)) for t in range(0, N, tile_n)]
     rows = np.unique(np.concatenate([[0, M - 1], per_r, rng.choice(M, min(nr, M), replace=False)]).astype(np.int64))
     cols = np.unique(np.concatenate([[0, N - 1], per_c, rng.choice(N, min(nc, N), replace=False)]).astype(np.int64))
     return rows, cols
