@@ -243,18 +243,46 @@ def test_per_token_codes_in_the_call_workspace(m, k, dt):
     order (rows padded to 16) written by the 16-row-tile quantizer where its
     registers hold a tile's rows (bf16 K <= 8192, fp32 K <= 4096), row-major
     codes beyond that (K = 8320); the scales follow at the next 256 bytes."""
-    from test_abi_host import pack_reference
-    from workloads import bf16_bits_from_f32
     rng = np.random.default_rng(m * 13 + k)
     x = (rng.standard_t(3, (m, k)) * 2).astype(np.float32)
     x[rng.integers(0, m, 3)] = 0.0                      # zero rows: unit scales
     x[:, rng.integers(0, k, 2)] *= 30
+    _check_call_workspace(x, dt, f"{m}x{k} {dt}")
+
+
+def test_per_token_edge_rows_in_the_call():
+    """The edge rows of the standalone per-token quantizer's test (zero and
+    signed-zero rows, rows whose scale leaves [2^-60, 2^60], huge rows, a
+    maximum at the last element, subnormals) quantized inside fp8_scaled_gemm
+    by the 16-row-tile quantizer (M > 32, K = 128), bf16 and fp32."""
+    k = 128
+    rng = np.random.default_rng(31)
+    rows = [np.zeros(k, np.float32)]
+    r = np.zeros(k, np.float32); r[::2] = -0.0; rows.append(r)
+    for scale in (1e-30, 1e-38, 3e-39, 2.0 ** -120, 1e25, 3e38, 1.0, 448.0):
+        rows.append((rng.standard_normal(k) * scale).astype(np.float32))
+    r = rng.standard_normal(k).astype(np.float32); r[-1] = 1000.0; rows.append(r)
+    rows.append(np.float32([2.0 ** -133 * i for i in range(k)]))
+    rows.append(np.float32([-(2.0 ** -130) * i for i in range(k)]))
+    rows += [(rng.standard_normal(k) * 1e-42).astype(np.float32) for _ in range(4)]   # fp32 subnormals
+    x = np.stack(rows + [rng.standard_normal(k).astype(np.float32) for _ in range(40 - len(rows))])
+    _check_call_workspace(x, "bf16", "edge rows bf16")
+    _check_call_workspace(x, "f32", "edge rows fp32")
+
+
+def _check_call_workspace(x, dt, what):
+    """Run a per-token fp8_scaled_gemm on x (quantized inside the call) and compare
+    the codes and scales its workspace holds with the oracle's, byte for byte."""
+    from test_abi_host import pack_reference
+    from workloads import bf16_bits_from_f32
+    m, k = x.shape
     if dt == "bf16":
         xb = bf16_bits_from_f32(x)
         xt, xf = dev_bf16(xb), f32_from_bf16_bits(xb)
     else:
         xt, xf = dev(x), x
     n = 16
+    rng = np.random.default_rng(k)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     wq_t, sw_t = sg.fp8_quant_weight_per_channel(dev(w))
     nbytes = sg.fp8_scaled_gemm_workspace_size(xt.dtype, "per_token", m, n, k)
@@ -268,12 +296,12 @@ def test_per_token_codes_in_the_call_workspace(m, k, dt):
     codes = wsh[:rows * k]
     if packed:
         live = pack_reference(np.ones((m, k), np.uint8)).astype(bool)
-        assert_codes_equal(codes[live], pack_reference(want_q)[live], f"{m}x{k} {dt} packed codes")
+        assert_codes_equal(codes[live], pack_reference(want_q)[live], f"{what} packed codes")
     else:
-        assert_codes_equal(codes.reshape(m, k), want_q, f"{m}x{k} {dt} row-major codes")
+        assert_codes_equal(codes.reshape(m, k), want_q, f"{what} row-major codes")
     off = (rows * k + 255) // 256 * 256
     got_s = wsh[off:off + 4 * m].view(np.float32)
-    assert np.array_equal(got_s.view(np.uint32), np.asarray(want_s, np.float32).view(np.uint32)), f"{m}x{k} {dt} scales"
+    assert np.array_equal(got_s.view(np.uint32), np.asarray(want_s, np.float32).view(np.uint32)), f"{what} scales"
 
 
 def _sample(M, N, seed, nr=40, nc=384, tile=256):
