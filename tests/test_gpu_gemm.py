@@ -334,12 +334,15 @@ def test_prefill_full_size_sampled(k, accum, layout):
 
 
 @pytest.mark.parametrize("accum", ACCUMS)
-@pytest.mark.parametrize("static", [True, False], ids=["static", "dynamic"])
-def test_large_layer_sampled(static, accum):
+@pytest.mark.parametrize("static,layout", [(True, "packed"), (False, "packed"), (False, "row_major")],
+                         ids=["static-packed", "dynamic-packed", "dynamic-row_major"])
+def test_large_layer_sampled(static, layout, accum):
+    """The large layer in the calls the benchmark times (bf16 X quantized inside
+    the call into the fragment order, packed W; per-token and static arms), and
+    the per-token arm on row-major W."""
     xb, w = large_layer_inputs()
     rows, cols = _sample(xb.shape[0], w.shape[0], 4, nr=24, nc=256)
     s = np.float32(STATIC_SCALE_NUM) / np.float32(STATIC_SCALE_DEN) if static else None
-    layout = "packed" if static else "row_major"
     gemm_case(xb, w, rows=rows, cols=cols, accum=accum, static=s, layout=layout,
               what=f"large {'static' if static else 'dyn'} {layout}")
 
