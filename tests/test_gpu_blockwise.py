@@ -172,7 +172,8 @@ def test_decode(m, accum):
 @pytest.mark.parametrize("kmajor", [False, True], ids=["scales_row_major", "scales_kmajor"])
 @pytest.mark.parametrize("layout", ["row_major", "packed"])
 @pytest.mark.parametrize("m,n,k", [(300, 1000, 1024), (129, 1001, 256), (33, 4100, 512), (17, 515, 128),
-                                   (1, 7, 128), (5, 1, 384), (256, 384, 2048), (520, 130, 384)])
+                                   (1, 7, 128), (5, 1, 384), (256, 384, 2048), (520, 130, 384), (300, 257, 128),
+                                   (65, 1000, 256)])
 def test_ragged(m, n, k, layout, kmajor):
     rng = np.random.default_rng(m * 7 + n + k)
     x = rng.standard_normal((m, k)).astype(np.float32)
