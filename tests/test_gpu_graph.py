@@ -109,3 +109,56 @@ def test_decode_step_replays_bit_exact():
         for name in e_outs:
             assert torch.equal(g_outs[name].view(torch.int16), e_outs[name].view(torch.int16)), (rep, name)
         assert torch.equal(kc, k_cache) and torch.equal(vc, v_cache), rep
+
+
+def test_prefill_calls_replay_bit_exact():
+    """Prefill-sized calls captured and replayed: fp8_scaled_gemm on bf16
+    activations with the per-token quantization inside the call (the 16-row-tile
+    quantizer into the fragment order, then the large-tile exact GEMM) and with a
+    given per-tensor scale, and the block-wise GEMM with exact partials on
+    pre-quantized codes; every replay on new inputs equals the eager calls bit
+    for bit."""
+    rng = np.random.default_rng(6)
+    M, N, K = 300, 1000, 1024
+    w = dev((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wq, sw = sg.fp8_quant_weight_per_channel(w)
+    wp = sg.fp8_pack_weights(wq)
+    wbq, wbs = sg.fp8_quant_weight_blockwise(w)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    st = torch.tensor([0.011], dtype=torch.float32, device="cuda")
+    ws_pt = torch.empty((sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_token", M, N, K),), dtype=torch.uint8,
+                        device="cuda")
+    ws_st = torch.empty((sg.fp8_scaled_gemm_workspace_size(torch.bfloat16, "per_tensor", M, N, K),),
+                        dtype=torch.uint8, device="cuda")
+    aq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+
+    def step(o):
+        sg.fp8_scaled_gemm(x, None, wp, sw, y=o["pt"], workspace=ws_pt, w_layout="packed")
+        sg.fp8_scaled_gemm(x, st, wp, sw, y=o["st"], workspace=ws_st, a_scale_mode="per_tensor", w_layout="packed")
+        sg.fp8_quant_per_token_group(x, q=aq, scales=sa)
+        sg.fp8_scaled_gemm_blockwise(aq, sa, wbq, wbs, y=o["bw"], accum="exact")
+
+    def new_outs():
+        return {k: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for k in ("pt", "st", "bw")}
+
+    g_outs = new_outs()
+    x.copy_(_bf16(rng, (M, K)))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(g_outs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(g_outs)
+    for rep in range(4):
+        x.copy_(_bf16(np.random.default_rng(200 + rep), (M, K), 2.0))
+        g.replay()
+        torch.cuda.synchronize()
+        e_outs = new_outs()
+        step(e_outs)
+        torch.cuda.synchronize()
+        for name in e_outs:
+            assert torch.equal(g_outs[name].view(torch.int16), e_outs[name].view(torch.int16)), (rep, name)
