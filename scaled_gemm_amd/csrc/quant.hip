@@ -305,57 +305,99 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return t;
 }
 
-template <typename InT, int kChunks, bool kPacked>
+// One workgroup per row; each thread holds kUnits 16-element units of x as
+// raw words through the sum of squares, then the normalised values through the
+// row maximum and the encode (16-byte loads, 16-byte non-temporal code stores,
+// as in row_quant_units).  The sum of squares takes 16 kUnits sequential fused
+// multiply-adds per thread, then the wave tree and the fixed-order sum of the
+// four waves.
+template <typename InT, int kUnits, bool kPacked>
 __global__ __launch_bounds__(256) void rmsnorm_quant(const InT* __restrict__ x, const InT* __restrict__ gamma,
                                                      float eps, int64_t K, uint8_t* __restrict__ q,
                                                      float* __restrict__ scales, float* __restrict__ y_out) {
+    constexpr int kWords = (int)sizeof(InT);      // 16-byte words per unit: 2 (bf16) or 4 (fp32)
+    constexpr int kPerWord = 16 / kWords;          // elements per word
     __shared__ float red[4];
-    const int t = (int)threadIdx.x;
     const int64_t row = blockIdx.x;
     const InT* xr = x + row * K;
-    const int nchunks = (int)(K >> 3);
-    float v[kChunks][8];
+    const int nunits = (int)(K >> 4);
+    auto unpack = [](const uint4 (&w)[kWords], float (&v)[16]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) {
+            const uint4 a = w[i];
+            if constexpr (kWords == 2) {
+                v[8 * i + 0] = bf16_lo(a.x); v[8 * i + 1] = bf16_hi(a.x); v[8 * i + 2] = bf16_lo(a.y);
+                v[8 * i + 3] = bf16_hi(a.y); v[8 * i + 4] = bf16_lo(a.z); v[8 * i + 5] = bf16_hi(a.z);
+                v[8 * i + 6] = bf16_lo(a.w); v[8 * i + 7] = bf16_hi(a.w);
+            } else {
+                v[4 * i + 0] = __uint_as_float(a.x); v[4 * i + 1] = __uint_as_float(a.y);
+                v[4 * i + 2] = __uint_as_float(a.z); v[4 * i + 3] = __uint_as_float(a.w);
+            }
+        }
+    };
+    uint4 r[kUnits][kWords];
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+        const int u = threadIdx.x + 256 * i;
+        if (u < nunits) {
+#pragma unroll
+            for (int w = 0; w < kWords; ++w)
+                r[i][w] = *reinterpret_cast<const uint4*>(xr + (int64_t)u * 16 + w * kPerWord);
+        }
+    }
     float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-        const int c = t + i * 256;
-        if (c < nchunks) {
-            load_chunk<InT>(xr + (int64_t)c * 8, v[i]);
+    for (int i = 0; i < kUnits; ++i) {
+        if ((int)threadIdx.x + 256 * i < nunits) {
+            float v[16];
+            unpack(r[i], v);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(v[i][j], v[i][j], ss);
+            for (int j = 0; j < 16; ++j) ss = __builtin_fmaf(v[j], v[j], ss);
         }
     }
     ss = block_sum(ss, red);
-    const float r = 1.0f / __builtin_sqrtf(ss / (float)K + eps);
+    const float rs = 1.0f / __builtin_sqrtf(ss / (float)K + eps);
+    float y[kUnits][16];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-        const int c = t + i * 256;
-        if (c < nchunks) {
-            float g[8];
-            load_chunk<InT>(gamma + (int64_t)c * 8, g);
+    for (int i = 0; i < kUnits; ++i) {
+        const int u = threadIdx.x + 256 * i;
+        if (u < nunits) {
+            uint4 gw[kWords];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                v[i][j] = (v[i][j] * r) * g[j];
-                amax = fmaxf(amax, __builtin_fabsf(v[i][j]));
+            for (int w = 0; w < kWords; ++w)
+                gw[w] = *reinterpret_cast<const uint4*>(gamma + (int64_t)u * 16 + w * kPerWord);
+            float v[16], g[16];
+            unpack(r[i], v);
+            unpack(gw, g);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                y[i][j] = (v[j] * rs) * g[j];
+                amax = fmaxf(amax, __builtin_fabsf(y[i][j]));
             }
             if (y_out) {
-                float4* yo = reinterpret_cast<float4*>(y_out + row * K + (int64_t)c * 8);
-                yo[0] = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
-                yo[1] = make_float4(v[i][4], v[i][5], v[i][6], v[i][7]);
+                float4* yo = reinterpret_cast<float4*>(y_out + row * K + (int64_t)u * 16);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    yo[j] = make_float4(y[i][4 * j], y[i][4 * j + 1], y[i][4 * j + 2], y[i][4 * j + 3]);
             }
         }
     }
     amax = block_max(amax, red);
     const float s = dynamic_scale(amax, kE4M3Max);
-    if (t == 0) scales[row] = s;
+    if (threadIdx.x == 0) scales[row] = s;
     const QScale p = make_qscale(s, kE4M3Max);
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-        const int c = t + i * 256;
-        if (c < nchunks) {
-            uint8_t* dst = kPacked ? q + packed_offset(row, (int64_t)c * 8, K >> 7) : q + row * K + (int64_t)c * 8;
-            store8_stream(dst, encode_chunk_dynamic<float>(v[i], p));
+    for (int i = 0; i < kUnits; ++i) {
+        const int u = threadIdx.x + 256 * i;
+        if (u < nunits) {
+            float lo[8], hi[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { lo[j] = y[i][j]; hi[j] = y[i][8 + j]; }
+            const uint2 c0 = encode_chunk_dynamic<float>(lo, p), c1 = encode_chunk_dynamic<float>(hi, p);
+            const int64_t k = (int64_t)u * 16;
+            uint8_t* dst = kPacked ? q + packed_offset(row, k, K >> 7) : q + row * K + k;
+            store16_stream(dst, make_uint4(c0.x, c0.y, c1.x, c1.y));
         }
     }
 }
@@ -363,12 +405,11 @@ __global__ __launch_bounds__(256) void rmsnorm_quant(const InT* __restrict__ x, 
 template <typename InT, bool kPacked>
 static void launch_rmsnorm_quant_t(const InT* x, const InT* g, float eps, int64_t M, int64_t K, uint8_t* q,
                                    float* scales, float* y_out, hipStream_t stream) {
-    const int64_t per = (K / 8 + 255) / 256;
+    const int64_t per = (K / 16 + 255) / 256;   // units per thread (K <= 16384: at most 4)
     dim3 grid((unsigned)M), block(256);
     if (per <= 1) rmsnorm_quant<InT, 1, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
     else if (per <= 2) rmsnorm_quant<InT, 2, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
-    else if (per <= 4) rmsnorm_quant<InT, 4, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
-    else rmsnorm_quant<InT, 8, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
+    else rmsnorm_quant<InT, 4, kPacked><<<grid, block, 0, stream>>>(x, g, eps, K, q, scales, y_out);
 }
 
 hipError_t launch_rmsnorm_quant(const void* x, bool x_is_bf16, const void* gamma, float eps, int64_t M, int64_t K,
