@@ -34,6 +34,18 @@ __device__ __forceinline__ int64_t packed_offset(int64_t m, int64_t k, int64_t n
     return (((m >> 4) * nkb + (k >> 7)) << 11) + ((j >> 4) & 1) * 1024 + (((m & 15) + 16 * (j >> 5)) << 4) + (j & 15);
 }
 
+// The 16 elements of a unit as two chunks of 8 (loads issued before any use).
+template <typename InT, bool kStream>
+__device__ __forceinline__ void load_unit(const InT* p, float (&v)[8], float (&w)[8]) {
+    if (kStream) {
+        load_chunk_stream<InT>(p, v);
+        load_chunk_stream<InT>(p + 8, w);
+    } else {
+        load_chunk<InT>(p, v);
+        load_chunk<InT>(p + 8, w);
+    }
+}
+
 // One workgroup of 256 threads per row; thread t holds units t, t + 256, ...
 // (kUnits of them, 16 consecutive elements each) as raw words between the
 // maximum and the encode, so X is read once.  Each unit's 16 codes leave in one
@@ -432,58 +444,125 @@ hipError_t launch_rmsnorm_quant(const void* x, bool x_is_bf16, const void* gamma
 // ---------------------------------------------------------------------------
 // Block-wise dynamic quantization.
 //
-// Activations, one scale per (row, 128-element group): a group is 16 chunks of
-// 8 elements, one chunk per thread, so the 16 threads of a group take its
-// maximum with four shuffles and each encodes its own chunk.  The grid strides
-// over chunks in multiples of 16 and the chunk count is a multiple of 16
-// (K % 128 == 0), so a group's 16 threads are always active together.
+// Activations, one scale per (row, 128-element group): a group is 8 units of
+// 16 elements, one unit per thread (two 16-byte loads for bf16), so the 8
+// threads of a group take its maximum with three shuffles and each encodes its
+// own unit into one 16-byte non-temporal store.  Units per row are a multiple
+// of 8 (K % 128 == 0), and the grid strides over units in multiples of 256, so
+// a group's 8 threads are always active together (the shuffles stay inside the
+// group).  The grid covers every unit once up to 2^28 units.  Row-major codes
+// (the fragment order: group_quant_packed below).
 // scales[m * (K / 128) + g] = RN32(amax / 448) (1.0 for an all-zero group).
-template <typename InT, bool kPacked>
-__global__ __launch_bounds__(256) void group_quant(const InT* __restrict__ x, int64_t K, int64_t nchunks,
+template <typename InT>
+__global__ __launch_bounds__(256) void group_quant(const InT* __restrict__ x, int64_t K, int64_t nunits,
                                                    uint8_t* __restrict__ q, float* __restrict__ scales, int64_t M,
                                                    int kmajor) {
+    constexpr int kWords = (int)sizeof(InT);      // 16-byte words per unit: 2 (bf16) or 4 (fp32)
+    constexpr int kPerWord = 16 / kWords;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
-        float v[8];
-        load_chunk<InT>(x + c * 8, v);
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += stride) {
+        uint4 w[kWords];
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) w[i] = *reinterpret_cast<const uint4*>(x + u * 16 + i * kPerWord);
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) {
+            const uint4 a = w[i];
+            if constexpr (kWords == 2) {
+                v[8 * i + 0] = bf16_lo(a.x); v[8 * i + 1] = bf16_hi(a.x); v[8 * i + 2] = bf16_lo(a.y);
+                v[8 * i + 3] = bf16_hi(a.y); v[8 * i + 4] = bf16_lo(a.z); v[8 * i + 5] = bf16_hi(a.z);
+                v[8 * i + 6] = bf16_lo(a.w); v[8 * i + 7] = bf16_hi(a.w);
+            } else {
+                v[4 * i + 0] = __uint_as_float(a.x); v[4 * i + 1] = __uint_as_float(a.y);
+                v[4 * i + 2] = __uint_as_float(a.z); v[4 * i + 3] = __uint_as_float(a.w);
+            }
+        }
         float amax = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+        for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
         const float s = dynamic_scale(amax, kE4M3Max);
-        if ((c & 15) == 0) {
-            // group g = c / 16 is (row g / nkb, k block g % nkb): row-major [M, K/128] or k-block-major [K/128, M]
-            const int64_t g = c >> 4, nkb = K >> 7;
+        if ((u & 7) == 0) {
+            // group g = u / 8 is (row g / nkb, k block g % nkb): row-major [M, K/128] or k-block-major [K/128, M]
+            const int64_t g = u >> 3, nkb = K >> 7;
             scales[kmajor ? (g % nkb) * M + g / nkb : g] = s;
         }
         const QScale p = make_qscale(s, kE4M3Max);
-        uint8_t* dst;
-        if (kPacked) {
-            const int64_t e = c * 8, m = e / K;
-            dst = q + packed_offset(m, e - m * K, K >> 7);
-        } else {
-            dst = q + c * 8;
-        }
-        *reinterpret_cast<uint2*>(dst) = encode_chunk_dynamic<InT>(v, p);
+        float lo[8], hi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { lo[j] = v[j]; hi[j] = v[8 + j]; }
+        const uint2 c0 = encode_chunk_dynamic<InT>(lo, p), c1 = encode_chunk_dynamic<InT>(hi, p);
+        store16_stream(q + u * 16, make_uint4(c0.x, c0.y, c1.x, c1.y));
+    }
+}
+
+// The same rule written straight into the fragment order: thread t takes lane
+// slot l = t % 64 of fragment block b = t / 64 (16-row tile b / nkb, k block
+// b % nkb), i.e. the 32 elements of row 16 (b / nkb) + l % 16 at
+// 128 (b % nkb) + 32 (l / 16), whose codes are the lane's two 16-byte halves.
+// A group (row, k block) is the four lanes l % 16 of one wave (two shuffles),
+// and every store instruction writes a contiguous kilobyte.  Rows past M are
+// read as row M - 1 and not written.
+template <typename InT>
+__global__ __launch_bounds__(256) void group_quant_packed(const InT* __restrict__ x, int64_t M, int64_t K,
+                                                          uint8_t* __restrict__ q, float* __restrict__ scales,
+                                                          int kmajor) {
+    const int64_t nkb = K >> 7;
+    const int64_t nthreads = ((M + 15) >> 4) * nkb * 64;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;   // a multiple of 64: waves stay whole
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nthreads; t += stride) {
+        const int64_t b = t >> 6;
+        const int l = (int)(t & 63);
+        const int64_t kb = b % nkb;
+        int64_t m = ((b / nkb) << 4) + (l & 15);
+        const bool live = m < M;
+        m = live ? m : M - 1;
+        const InT* src = x + m * K + kb * 128 + 32 * (l >> 4);
+        float v0[8], v1[8], v2[8], v3[8];
+        load_unit<InT, false>(src, v0, v1);
+        load_unit<InT, false>(src + 16, v2, v3);
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            amax = fmaxf(amax, fmaxf(fmaxf(__builtin_fabsf(v0[j]), __builtin_fabsf(v1[j])),
+                                     fmaxf(__builtin_fabsf(v2[j]), __builtin_fabsf(v3[j]))));
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const float s = dynamic_scale(amax, kE4M3Max);
+        if (!live) continue;
+        if (l < 16) scales[kmajor ? kb * M + m : m * nkb + kb] = s;
+        const QScale p = make_qscale(s, kE4M3Max);
+        const uint2 c0 = encode_chunk_dynamic<InT>(v0, p), c1 = encode_chunk_dynamic<InT>(v1, p);
+        const uint2 c2 = encode_chunk_dynamic<InT>(v2, p), c3 = encode_chunk_dynamic<InT>(v3, p);
+        uint8_t* dst = q + (b << 11) + (l << 4);
+        store16_stream(dst, make_uint4(c0.x, c0.y, c1.x, c1.y));
+        store16_stream(dst + 1024, make_uint4(c2.x, c2.y, c3.x, c3.y));
     }
 }
 
 hipError_t launch_group_quant(const void* x, bool x_is_bf16, int64_t M, int64_t K, uint8_t* q, float* scales,
                               bool packed, bool scales_kmajor, hipStream_t stream) {
-    const int64_t nchunks = M * (K / 8);
-    if (nchunks == 0) return hipSuccess;
-    int64_t blocks = (nchunks + 255) / 256;
-    if (blocks > 256 * 16) blocks = 256 * 16;
-    dim3 grid((unsigned)blocks), block(256);
+    if (M == 0 || K == 0) return hipSuccess;
     const int km = scales_kmajor ? 1 : 0;
-    if (x_is_bf16) {
-        if (packed) group_quant<uint16_t, true><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nchunks, q, scales, M, km);
-        else group_quant<uint16_t, false><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nchunks, q, scales, M, km);
-    } else {
-        if (packed) group_quant<float, true><<<grid, block, 0, stream>>>((const float*)x, K, nchunks, q, scales, M, km);
-        else group_quant<float, false><<<grid, block, 0, stream>>>((const float*)x, K, nchunks, q, scales, M, km);
+    if (packed) {
+        const int64_t nthreads = ((M + 15) / 16) * (K / 128) * 64;
+        // small calls (decode rows) in 64-thread workgroups: more of them to spread over the chip
+        const int tpb = nthreads < ((int64_t)1 << 16) ? 64 : 256;
+        int64_t blocks = (nthreads + tpb - 1) / tpb;
+        if (blocks > ((int64_t)1 << 20)) blocks = (int64_t)1 << 20;
+        dim3 grid((unsigned)blocks), block((unsigned)tpb);
+        if (x_is_bf16) group_quant_packed<uint16_t><<<grid, block, 0, stream>>>((const uint16_t*)x, M, K, q, scales, km);
+        else group_quant_packed<float><<<grid, block, 0, stream>>>((const float*)x, M, K, q, scales, km);
+        return hipGetLastError();
     }
+    const int64_t nunits = M * (K / 16);
+    const int tpb = nunits < ((int64_t)1 << 16) ? 64 : 256;
+    int64_t blocks = (nunits + tpb - 1) / tpb;
+    if (blocks > ((int64_t)1 << 20)) blocks = (int64_t)1 << 20;
+    dim3 grid((unsigned)blocks), block((unsigned)tpb);
+    if (x_is_bf16) group_quant<uint16_t><<<grid, block, 0, stream>>>((const uint16_t*)x, K, nunits, q, scales, M, km);
+    else group_quant<float><<<grid, block, 0, stream>>>((const float*)x, K, nunits, q, scales, M, km);
     return hipGetLastError();
 }
 
@@ -559,18 +638,6 @@ __device__ __forceinline__ uint4 encode16_given(const float (&v)[8], const float
         return o;
     };
     return sc.fast ? enc(std::true_type{}) : enc(std::false_type{});
-}
-
-// The 16 elements of a unit as two chunks of 8 (loads issued before any use).
-template <typename InT, bool kStream>
-__device__ __forceinline__ void load_unit(const InT* p, float (&v)[8], float (&w)[8]) {
-    if (kStream) {
-        load_chunk_stream<InT>(p, v);
-        load_chunk_stream<InT>(p + 8, w);
-    } else {
-        load_chunk<InT>(p, v);
-        load_chunk<InT>(p + 8, w);
-    }
 }
 
 // One 16-element unit per thread: the loads go out first, then the unit's
@@ -678,7 +745,7 @@ hipError_t launch_static_quant_packed(const void* x, bool x_is_bf16, int64_t M, 
     if (M == 0 || K == 0) return hipSuccess;
     const int64_t nthreads = ((M + 15) / 16) * (K / 128) * 64;
     int64_t blocks = (nthreads + 255) / 256;
-    if (blocks > ((int64_t)1 << 31) - 1) blocks = ((int64_t)1 << 31) - 1;
+    if (blocks > ((int64_t)1 << 20)) blocks = (int64_t)1 << 20;   // the loop strides over the rest
     dim3 grid((unsigned)blocks), block(256);
     if (x_is_bf16) static_quant_packed<uint16_t><<<grid, block, 0, stream>>>((const uint16_t*)x, M, K, scale, q);
     else static_quant_packed<float><<<grid, block, 0, stream>>>((const float*)x, M, K, scale, q);
