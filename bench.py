@@ -699,30 +699,29 @@ def run_details(sg, torch, dev, to_bf16, T, wanted, clock):
             xb, w, _ = prefill_inputs(K)
             M, N = xb.shape[0], w.shape[0]
             xl = copies(to_bf16(xb), 2)
-            # the activation scales k-block-major ([K/128, M]): the large-tile kernel then copies the
-            # scales of 64 rows of one k block as one contiguous run
-            aq, sa = sg.fp8_quant_per_token_group(xl[0], scale_layout="kmajor")
-            d = T.per_call(lambda i: sg.fp8_quant_per_token_group(xl[i % 2], q=aq, scales=sa, scale_layout="kmajor"))
-            out.append(gbs_row(f"block-wise act quant 1x128 X bf16 [{M},{K}] (k-block-major scales)", d,
-                               3 * M * K + 4 * M * (K // 128)))
+            # the codes in the fragment order and the activation scales k-block-major ([K/128, M]): the
+            # large-tile kernels then copy whole 2 KB blocks of A and the scales of 64 rows of one k block
+            # as one contiguous run
+            aq, sa = sg.fp8_quant_per_token_group(xl[0], layout="packed", scale_layout="kmajor")
+            d = T.per_call(lambda i: sg.fp8_quant_per_token_group(xl[i % 2], layout="packed", q=aq, scales=sa,
+                                                                  scale_layout="kmajor"))
+            out.append(gbs_row(f"block-wise act quant 1x128 X bf16 [{M},{K}] (fragment order, k-block-major "
+                               f"scales)", d, 3 * M * K + 4 * M * (K // 128)))
             wq, sw = sg.fp8_quant_weight_blockwise(torch.from_numpy(w).to(dev))
             wp = sg.fp8_pack_weights(wq)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            d = T.per_call(lambda i: sg.fp8_scaled_gemm_blockwise(aq, sa, wp, sw, y=y, accum="mfma_fp8",
-                                                                  w_layout="packed", w_shape=(N, K),
-                                                                  a_scale_layout="kmajor"), min_calls=50)
-            out.append(tflops_row(f"block-wise prefill GEMM {M}x{N}x{K} (k-block-major activation scales)", d,
-                                  2.0 * M * N * K, "mfma_fp8"))
-            d = T.per_call(lambda i: sg.fp8_scaled_gemm_blockwise(aq, sa, wp, sw, y=y, accum="exact",
-                                                                  w_layout="packed", w_shape=(N, K),
-                                                                  a_scale_layout="kmajor"), min_calls=50)
-            out.append(tflops_row(f"block-wise prefill GEMM {M}x{N}x{K} exact partials (k-block-major activation "
-                                  f"scales)", d, 2.0 * M * N * K, "exact"))
+            for accum, tag in (("mfma_fp8", ""), ("exact", " exact partials")):
+                d = T.per_call(lambda i: sg.fp8_scaled_gemm_blockwise(aq, sa, wp, sw, y=y, accum=accum,
+                                                                      w_layout="packed", w_shape=(N, K),
+                                                                      a_layout="packed", a_shape=(M, K),
+                                                                      a_scale_layout="kmajor"), min_calls=50)
+                out.append(tflops_row(f"block-wise prefill GEMM {M}x{N}x{K}{tag} (packed A, k-block-major "
+                                      f"activation scales)", d, 2.0 * M * N * K, accum))
             aq2, sa2 = sg.fp8_quant_per_token_group(xl[0])
             d = T.per_call(lambda i: sg.fp8_scaled_gemm_blockwise(aq2, sa2, wp, sw, y=y, accum="mfma_fp8",
                                                                   w_layout="packed", w_shape=(N, K)), min_calls=50)
-            out.append(tflops_row(f"block-wise prefill GEMM {M}x{N}x{K} (row-major activation scales)", d,
-                                  2.0 * M * N * K, "mfma_fp8"))
+            out.append(tflops_row(f"block-wise prefill GEMM {M}x{N}x{K} (row-major A, row-major activation "
+                                  f"scales)", d, 2.0 * M * N * K, "mfma_fp8"))
             del xl, aq, sa, aq2, sa2, wq, wp, y
             torch.cuda.empty_cache()
 
