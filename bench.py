@@ -698,12 +698,13 @@ def run_details(sg, torch, dev, to_bf16, T, wanted, clock):
         for K in (4096, 14336):
             xb, w, _ = prefill_inputs(K)
             M, N = xb.shape[0], w.shape[0]
-            xl = copies(to_bf16(xb), 2)
+            # enough activation copies that the 256 MB last-level cache cannot serve the quantizer's reads
+            xl = copies(to_bf16(xb), 8 if K == 4096 else 3)
             # the codes in the fragment order and the activation scales k-block-major ([K/128, M]): the
             # large-tile kernels then copy whole 2 KB blocks of A and the scales of 64 rows of one k block
             # as one contiguous run
             aq, sa = sg.fp8_quant_per_token_group(xl[0], layout="packed", scale_layout="kmajor")
-            d = T.per_call(lambda i: sg.fp8_quant_per_token_group(xl[i % 2], layout="packed", q=aq, scales=sa,
+            d = T.per_call(lambda i: sg.fp8_quant_per_token_group(xl[i % len(xl)], layout="packed", q=aq, scales=sa,
                                                                   scale_layout="kmajor"))
             out.append(gbs_row(f"block-wise act quant 1x128 X bf16 [{M},{K}] (fragment order, k-block-major "
                                f"scales)", d, 3 * M * K + 4 * M * (K // 128)))
@@ -759,12 +760,13 @@ def run_details(sg, torch, dev, to_bf16, T, wanted, clock):
         for K in (4096, 14336):
             xb, w, _ = prefill_inputs(K)
             M, N = xb.shape[0], w.shape[0]
-            xl = copies(to_bf16(xb), 2)
+            # enough activation copies that the 256 MB last-level cache cannot serve the quantizer's reads
+            xl = copies(to_bf16(xb), 8 if K == 4096 else 3)
             wp, wsc = sg.fp8_quant_mx(torch.from_numpy(w).to(dev), layout="packed", scale_layout="packed")
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             for fmt in ("e4m3", "e5m2"):
                 aq, sa = sg.fp8_quant_mx(xl[0], fmt, layout="packed", scale_layout="packed")
-                d = T.per_call(lambda i: sg.fp8_quant_mx(xl[i % 2], fmt, layout="packed", scale_layout="packed",
+                d = T.per_call(lambda i: sg.fp8_quant_mx(xl[i % len(xl)], fmt, layout="packed", scale_layout="packed",
                                                          q=aq, scales=sa))
                 out.append(gbs_row(f"MX act quant X bf16 [{M},{K}] {fmt}", d, 3 * M * K + M * K // 32))
                 d = T.per_call(lambda i: sg.fp8_scaled_gemm_mx(aq, sa, wp, wsc, a_fmt=fmt, y=y, w_layout="packed",
