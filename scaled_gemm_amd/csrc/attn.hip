@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
     __shared__ float p_lds[4][kG][kBlk];
     __shared__ float w_m[4][kG], w_l[4][kG];
     __shared__ float w_o[4][kG][kAttnD];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = (int)(blockIdx.x % (unsigned)nchunk);
     const int bg = (int)(blockIdx.x / (unsigned)nchunk);
     const int g = bg % Hkv, b = bg / Hkv;
@@ -140,29 +140,34 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
     float m_run = -__builtin_inff(), l_run = 0.0f;  // for head jh (lanes with jh < kG)
 
     // K slices for the 4 score tiles and V slices for the 8 p.V steps of the
-    // block at t0 (positions past t_end clamped to the last valid one; their
-    // scores are masked).  The next block's loads are issued before the
-    // current block is computed.
+    // block at t0, addressed from the block's uniform base with 32-bit per-lane
+    // offsets; positions past t_end are clamped to the last valid one (their
+    // scores are masked).  The row stride (Hkv * 128 < 2^23 bytes) and the
+    // position within the block (< 64) multiply in 24 bits.
+    const uint32_t rs = (uint32_t)row_stride;
     auto load_block = [&](uint4 (&kr)[4][2], uint4 (&vr)[8], int t0) __attribute__((always_inline)) {
+        const int last = t_end - 1 - t0;   // the last valid position, relative to t0
+        const uint8_t* kbase = kb + (int64_t)t0 * row_stride;
+        const uint8_t* vbase = vb + (int64_t)t0 * row_stride;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            int t = t0 + 16 * i + jh;
-            t = t < t_end ? t : t_end - 1;
-            const uint4* p = reinterpret_cast<const uint4*>(kb + (int64_t)t * row_stride + 32 * kq);
+            const int r = 16 * i + jh < last ? 16 * i + jh : last;
+            const uint32_t off = (uint32_t)__umul24((uint32_t)r, rs) + (uint32_t)(32 * kq);
+            const uint4* p = reinterpret_cast<const uint4*>(kbase + (uint64_t)off);
             kr[i][0] = p[0];
             kr[i][1] = p[1];
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            int t = t0 + 8 * k + ps;
-            t = t < t_end ? t : t_end - 1;
-            vr[k] = *reinterpret_cast<const uint4*>(vb + (int64_t)t * row_stride + 16 * dg);
+            const int r = 8 * k + ps < last ? 8 * k + ps : last;
+            const uint32_t off = (uint32_t)__umul24((uint32_t)r, rs) + (uint32_t)(16 * dg);
+            vr[k] = *reinterpret_cast<const uint4*>(vbase + (uint64_t)off);
         }
     };
-    uint4 kr[4][2], vr[8];
-    if (t_begin + wave * kBlk < t_end) load_block(kr, vr, t_begin + wave * kBlk);
-    for (int t0 = t_begin + wave * kBlk; t0 < t_end; t0 += 4 * kBlk) {
-        uint4 kn[4][2], vn[8];
+    // One block with its fragments in (kr, vr); the block four blocks on (this
+    // wave's next one) is loaded into (kn, vn) first.
+    auto block = [&](uint4 (&kr)[4][2], uint4 (&vr)[8], uint4 (&kn)[4][2], uint4 (&vn)[8], int t0)
+        __attribute__((always_inline)) {
         if (t0 + 4 * kBlk < t_end) load_block(kn, vn, t0 + 4 * kBlk);
         // ---- scores: 4 tiles of 16 positions x 16 head columns
         float x[4][4];
@@ -190,6 +195,8 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
         bm = wave_max16(bm);
         const float m_new = fmaxf(m_run, bm);  // finite: every block has a valid position
         const float alpha = __expf(m_run - m_new);
+        // no head of the kv head raised its maximum: every rescale factor is 1 and o stays as it is
+        const bool rescale = __builtin_amdgcn_ballot_w64(jh < kG && m_new != m_run) != 0;
         float bs = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -205,17 +212,19 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
         bs = wave_sum16(bs);
         l_run = alpha * l_run + bs;
         m_run = m_new;
-        // every lane needs each head's rescale factor: lane h holds it
-        float al[kG];
+        if (rescale) {
+            // every lane needs each head's rescale factor: lane h holds it
+            float al[kG];
 #pragma unroll
-        for (int h = 0; h < kG; ++h) al[h] = __shfl(alpha, h, 64);
+            for (int h = 0; h < kG; ++h) al[h] = __shfl(alpha, h, 64);
+#pragma unroll
+            for (int h = 0; h < kG; ++h)
+#pragma unroll
+                for (int d = 0; d < 16; ++d) o[h][d] *= al[h];
+        }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's p values are in LDS
         // ---- p.V for this wave's 64 positions
-#pragma unroll
-        for (int h = 0; h < kG; ++h)
-#pragma unroll
-            for (int d = 0; d < 16; ++d) o[h][d] *= al[h];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             float v[16];
@@ -228,6 +237,12 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
             }
         }
         __builtin_amdgcn_wave_barrier();
+    };
+    uint4 kr[4][2], vr[8];
+    if (t_begin + wave * kBlk < t_end) load_block(kr, vr, t_begin + wave * kBlk);
+    for (int t0 = t_begin + wave * kBlk; t0 < t_end; t0 += 4 * kBlk) {
+        uint4 kn[4][2], vn[8];
+        block(kr, vr, kn, vn, t0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             kr[i][0] = kn[i][0];
