@@ -476,11 +476,12 @@ def test_exact_mode_widens_every_code(m, layout):
 
 
 @pytest.mark.parametrize("accum", ACCUMS)
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 4, 20, 300])
 def test_empty_reduction(m, accum):
     """K = 0: an empty sum.  bf16 per-token activations with M <= 4 take the
     two-kernel path (the row quantizer writes the unit scales), never the
-    decode kernel that quantizes inside the GEMM; every output is 0."""
+    decode kernel that quantizes inside the GEMM; M = 20 runs the two-m-tile
+    decode kernel and M = 300 the large-tile kernels; every output is 0."""
     n = 40
     x = torch.empty((m, 0), dtype=torch.bfloat16, device="cuda")
     wq = torch.empty((n, 0), dtype=torch.uint8, device="cuda")

@@ -232,14 +232,15 @@ def test_decode_path_quantized_on_the_gpu():
     assert (np.abs(host(y)[:, cols].astype(np.float64) - exact) <= bound).all()
 
 
-def test_zero_depth_and_empty():
-    a = torch.zeros((3, 0), dtype=torch.uint8, device="cuda")
+@pytest.mark.parametrize("m", [3, 300], ids=["decode_kernel", "large_tile_kernel"])
+def test_zero_depth_and_empty(m):
+    a = torch.zeros((m, 0), dtype=torch.uint8, device="cuda")
     w = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
     e = torch.zeros((0,), dtype=torch.uint8, device="cuda")
-    y = torch.full((3, 5), 7.0, dtype=torch.float32, device="cuda")
+    y = torch.full((m, 5), 7.0, dtype=torch.float32, device="cuda")
     lib = sg.lib()
     st = lib.fp8_scaled_gemm_mx(a.data_ptr(), e.data_ptr(), sg.E4M3, w.data_ptr(), e.data_ptr(), 0, y.data_ptr(),
-                                sg.F32, 3, 5, 0, None)
+                                sg.F32, m, 5, 0, None)
     torch.cuda.synchronize()
     assert st == 0 and (host(y) == 0).all()
 
