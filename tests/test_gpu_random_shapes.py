@@ -1,5 +1,5 @@
 """Seeded random shapes through the GEMM paths whose tiling changed most often:
-fp8_scaled_gemm on bf16 activations quantized inside the call (per token: the
+fp8_scaled_gemm on bf16 (every fourth case fp32) activations quantized inside the call (per token: the
 16-row-tile quantizer into the fragment order above 32 rows; per tensor: the
 fragment-order static quantizer) and the block-wise GEMM in both accumulation
 modes.  Every output is compared with the oracle by the checkers of the
@@ -27,11 +27,11 @@ def _shape(rng):
     return m, n, k
 
 
-def _inputs(rng, m, n, k):
+def _inputs(rng, m, n, k, fp32=False):
     x = (rng.standard_t(4, (m, k)) * rng.uniform(0.5, 4)).astype(np.float32)
     x[:, rng.integers(0, k, 2)] *= 25
     w = (rng.standard_normal((n, k)) * 0.03).astype(np.float32)
-    return bf16_bits_from_f32(x), w
+    return (x if fp32 else bf16_bits_from_f32(x)), w
 
 
 @pytest.mark.parametrize("seed", range(32))
@@ -39,7 +39,7 @@ def test_scaled_gemm_random_shapes(seed):
     from test_gpu_gemm import gemm_case
     rng = np.random.default_rng(1000 + seed)
     m, n, k = _shape(rng)
-    xb, w = _inputs(rng, m, n, k)
+    xb, w = _inputs(rng, m, n, k, fp32=(seed % 4 == 1))   # fp32 activations every fourth case
     accum = ("exact", "mfma_fp8")[seed % 2]
     layout = ("packed", "row_major")[(seed // 2) % 2]
     static = np.float32(rng.uniform(0.005, 0.05)) if seed % 3 == 0 else None
