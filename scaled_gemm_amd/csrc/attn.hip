@@ -297,9 +297,10 @@ __global__ __launch_bounds__(256) void attn_split(const uint16_t* __restrict__ q
 }
 
 // Workgroup (b, h), one thread per dimension: the chunks' partials in chunk
-// order.  The chunk maxima and sums are first read by all threads at once (one
-// chunk per thread) and their weights exp(m_c - M) kept in LDS; then each
-// thread adds its dimension of the chunks' outputs, 8 chunks per batch of loads.
+// order.  The chunk maxima and sums are read by all threads at once (one chunk
+// per thread) and their weights exp(m_c - M) kept in LDS; each thread adds its
+// dimension of the chunks' outputs, the first 32 chunks' values loaded together
+// with the maxima and sums, any further chunks 8 per batch of loads.
 constexpr int kMaxChunks = 1024;  // S_cap <= 2^20
 
 template <bool kOutBf16>
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
                                                     const int32_t* __restrict__ lengths, int S_cap, int Hkv, int G,
                                                     int nchunk, void* __restrict__ out) {
     __shared__ float wgt[kMaxChunks];
+    __shared__ float lsm[kMaxChunks];
     __shared__ float red[2];
     const int h = (int)(blockIdx.x % (unsigned)(Hkv * G));
     const int b = (int)(blockIdx.x / (unsigned)(Hkv * G));
@@ -317,13 +319,21 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
     const int nc = (L + kChunk - 1) / kChunk;
     const size_t stride = (size_t)G * kPartFloats;
     const float* pb = part + ((size_t)(b * Hkv + g) * nchunk) * stride + (size_t)j * kPartFloats;
-    // chunk maxima -> M (every chunk c < nc holds at least one position, so its m is finite)
+    // The loads go out together: this thread's dimension of the first kPre chunks'
+    // outputs (they do not depend on the maxima) and the maximum and sum of chunk
+    // d (and d + 128, ...), so the kernel waits for memory about once.
+    constexpr int kPre = 32;
+    float ov[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) ov[u] = u < nc ? pb[(size_t)u * stride + d] : 0.0f;
     float mx = -__builtin_inff();
     for (int c = d; c < nc; c += blockDim.x) {
         const float m = pb[(size_t)c * stride + kAttnD];
         wgt[c] = m;
+        lsm[c] = pb[(size_t)c * stride + kAttnD + 1];
         mx = fmaxf(mx, m);
     }
+    // chunk maxima -> M (every chunk c < nc holds at least one position, so its m is finite)
     mx = wave_max(mx);
     if ((d & 63) == 0) red[d >> 6] = mx;
     __syncthreads();
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
     for (int c = d; c < nc; c += blockDim.x) {
         const float f = __expf(wgt[c] - M);
         wgt[c] = f;
-        ls += f * pb[(size_t)c * stride + kAttnD + 1];
+        ls += f * lsm[c];
     }
     ls = ls + __shfl_xor(ls, 32, 64);
     ls = ls + __shfl_xor(ls, 16, 64);
@@ -344,14 +354,18 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
     if ((d & 63) == 0) red[d >> 6] = ls;
     __syncthreads();
     const float lsum = red[0] + red[1];
+    // the weighted outputs in chunk order
     float acc = 0.0f;
-    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+        if (u < nc) acc += wgt[u] * ov[u];
+    int c = kPre;
     for (; c + 8 <= nc; c += 8) {
-        float ov[8];
+        float o8[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ov[u] = pb[(size_t)(c + u) * stride + d];
+        for (int u = 0; u < 8; ++u) o8[u] = pb[(size_t)(c + u) * stride + d];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc += wgt[c + u] * ov[u];
+        for (int u = 0; u < 8; ++u) acc += wgt[c + u] * o8[u];
     }
     for (; c < nc; ++c) acc += wgt[c] * pb[(size_t)c * stride + d];
     const float r = nc > 0 ? (acc / lsum) * v_scales[g] : 0.0f;
